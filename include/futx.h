@@ -1,0 +1,254 @@
+/*
+ * futx -- INT4 decode step of a Llama-style Transformer block on AMD Instinct
+ * MI355X (gfx950).  C ABI of libfutx.so.
+ *
+ * Sources.  The method is described by web pages about FuTransformer
+ * ("FP8 prefill and INT4 decode for Llama-style inference on Hopper"):
+ *   [ABS]  the paper's English abstract (airebao.com item page);
+ *   [INT4] kongchang.com/en article, section "INT4 Decode: letting
+ *          dequantization feed directly into MMA operands";
+ *   [FP8]  same article, section "FP8 Prefill: fusing GEMM and epilogue all
+ *          the way";
+ *   [ACC]  same article, section "Accuracy cost: perplexity from 6.24 to 7.23".
+ * The decode block uses INT4 projection weights and an INT4 KV-cache copy
+ * [ABS]; weights and keys are stored so that dequantized values feed the
+ * matrix cores directly, without an intermediate tile in memory [ABS, INT4];
+ * a block-diagonal Hadamard rotation reduces cache quantization error from
+ * outlier channels [ABS]; the RMSNorm gain is folded into the weights that
+ * follow the norm [ABS, FP8]; weights are rounded to nearest [ACC].
+ *
+ * Conventions (all entry points):
+ *  - Every buffer is owned by the caller.  The library allocates no device
+ *    memory and keeps no pointer after the call returns.
+ *  - "dev" pointers are device memory of the current HIP device; "host"
+ *    pointers are host memory.  `stream` is a hipStream_t (NULL = the null
+ *    stream).  Device work is enqueued asynchronously on `stream` unless the
+ *    entry point says otherwise.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    negative status nothing has been enqueued and futx_last_error() returns
+ *    a message (thread-local).  Device-side metadata (lengths, block tables,
+ *    slots, token ids) is trusted: out-of-range values are undefined
+ *    behaviour.
+ *  - No C++ exception crosses the ABI.  Calls are reentrant; calls on one
+ *    stream run in order.
+ *
+ * Number formats:
+ *  - bf16 / fp16 buffers are passed as uint16_t bit patterns.
+ *  - INT4 codes are symmetric, in [-8, 7]; a group of `w_group` input
+ *    channels of one weight row shares one fp16 scale = fp16(max|w| / 7)
+ *    (fp32 arithmetic, round to nearest even) and codes are
+ *    clamp(rint(w / scale), -8, 7) with the stored scale as divisor.  The KV
+ *    cache uses the same recipe with one scale per (token, KV head) over all
+ *    head_dim channels, saturated at 65504.
+ */
+#ifndef FUTX_H
+#define FUTX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t futx_status;
+#define FUTX_OK 0
+#define FUTX_E_ARG (-1)         /* null pointer, negative or inconsistent size */
+#define FUTX_E_UNSUPPORTED (-2) /* a shape or option the kernels do not support */
+#define FUTX_E_WORKSPACE (-3)   /* workspace smaller than required */
+#define FUTX_E_RANGE (-4)       /* a weight group scale overflows fp16 */
+#define FUTX_E_HIP (-5)         /* a HIP runtime call failed */
+
+/* Shape of one decoder block.  Supported: head_dim in {64, 128}; w_group in
+ * {64, 128}; had_block in {32, 64} dividing head_dim; page_size 64;
+ * hidden, n_heads*head_dim and intermediate multiples of 128 and of
+ * w_group; head_dim a multiple of w_group; n_heads a multiple of n_kv_heads
+ * with n_heads / n_kv_heads <= 16. */
+typedef struct futx_dims {
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;
+  int32_t w_group;   /* weight quantization group along the input dimension */
+  int32_t had_block; /* block size of the block-diagonal Hadamard rotation */
+  int32_t page_size; /* KV-cache tokens per page */
+  float rms_eps;     /* RMSNorm epsilon */
+  float rope_theta;  /* RoPE base */
+} futx_dims;
+
+/* The four projections of a block.  Logical weight matrices are row-major
+ * [N][K] fp32 (row n = output feature n, column k = input feature k):
+ *   QKV    N = (n_heads + 2 n_kv_heads) head_dim, K = hidden; rows are the
+ *          query heads, then the key heads, then the value heads, each head
+ *          head_dim consecutive rows.
+ *   O      N = hidden, K = n_heads head_dim.
+ *   GATEUP N = 2 intermediate, K = hidden; rows 0..I-1 are the gate
+ *          projection, rows I..2I-1 the up projection.
+ *   DOWN   N = hidden, K = intermediate. */
+typedef enum futx_proj {
+  FUTX_PROJ_QKV = 0,
+  FUTX_PROJ_O = 1,
+  FUTX_PROJ_GATEUP = 2,
+  FUTX_PROJ_DOWN = 3
+} futx_proj;
+
+/* Packed INT4 weights of one projection in device memory, in the order
+ * futx_pack_weights writes (opaque to callers; 256-byte aligned). */
+typedef struct futx_qweight {
+  const void* packed; /* futx_packed_sizes(...).packed_bytes bytes */
+  const void* scales; /* futx_packed_sizes(...).scale_bytes bytes (fp16) */
+} futx_qweight;
+
+typedef struct futx_block_weights {
+  futx_qweight qkv, o, gateup, down;
+} futx_block_weights;
+
+/* Paged INT4 KV cache of one layer (device memory, caller-owned).  Token t
+ * of a sequence lives in physical page block_table[t / page_size] at offset
+ * t % page_size; a "slot" is page * page_size + offset.  The code buffers
+ * hold the rotated keys and values in the order the attention kernel reads
+ * them (opaque; futx_kv_cache_sizes gives the sizes).  Scales are fp16
+ * [num_pages][n_kv_heads][page_size]. */
+typedef struct futx_kv_cache {
+  void* k_codes;
+  void* v_codes;
+  void* k_scales;
+  void* v_scales;
+  int32_t num_pages;
+} futx_kv_cache;
+
+/* Flags of futx_kv_append. */
+#define FUTX_KV_ROPE 1u     /* apply RoPE to keys at `positions` */
+#define FUTX_KV_HADAMARD 2u /* rotate keys and values by the block Hadamard */
+
+/* Last error message of this thread ("" if none). */
+const char* futx_last_error(void);
+
+/* ------------------------------------------------------------------ weights */
+
+/* Device bytes of a packed projection.  Source: INT4 projection weights
+ * with per-group scales [ABS, ACC]. */
+futx_status futx_packed_sizes(const futx_dims* dims, futx_proj proj, size_t* packed_bytes,
+                              size_t* scale_bytes);
+
+/* Offline weight packing.  Folds the RMSNorm gain into the weight columns
+ * (w'[n][k] = w[n][k] * gain[k], one fp32 multiply) when `gain_host` is not
+ * NULL [ABS, FP8], quantizes w' by the INT4 recipe above [ACC] and reorders
+ * nibbles and scales into the matrix-core operand order of the kernels
+ * [ABS, INT4].  w_host: fp32 [N][K] row-major (host).  gain_host: fp32 [K]
+ * or NULL (QKV takes the attention-norm gain, GATEUP the MLP-norm gain).
+ * Writes packed_dev / scales_dev (sizes from futx_packed_sizes) and returns
+ * after the copies have completed.  FUTX_E_RANGE if a scale overflows fp16. */
+futx_status futx_pack_weights(const futx_dims* dims, futx_proj proj, const float* w_host,
+                              const float* gain_host, void* packed_dev, void* scales_dev,
+                              void* stream);
+
+/* Same as futx_pack_weights but writes the device-order bytes to host
+ * buffers (no HIP call). */
+futx_status futx_pack_weights_host(const futx_dims* dims, futx_proj proj, const float* w_host,
+                                   const float* gain_host, void* packed_host, void* scales_host);
+
+/* Inverse of the device order (for tests): reads packed_dev / scales_dev and
+ * writes canonical bytes [N][K/2] (byte i of a row = code 2i in the low
+ * nibble, code 2i+1 in the high nibble, two's complement) and fp16 scales
+ * [N][K/w_group] in logical row order (host).  Blocks until done. */
+futx_status futx_unpack_weights(const futx_dims* dims, futx_proj proj, const void* packed_dev,
+                                const void* scales_dev, uint8_t* canon_bytes_host,
+                                uint16_t* canon_scales_host, void* stream);
+
+/* ----------------------------------------------------------------- KV cache */
+
+/* Bytes of each code buffer (k_codes and v_codes have the same size) and of
+ * each scale buffer for `num_pages` pages. */
+futx_status futx_kv_cache_sizes(const futx_dims* dims, int32_t num_pages, size_t* code_bytes,
+                                size_t* scale_bytes);
+
+/* Write n_tokens tokens into the INT4 cache [ABS]: for each token and KV
+ * head, keys get RoPE at positions[i] (FUTX_KV_ROPE), keys and values get
+ * the block-Hadamard rotation (FUTX_KV_HADAMARD) [ABS, INT4], then each is
+ * quantized per (token, KV head) and stored at slots[i].  flags = 0 stores
+ * the inputs as given (quantizer only).  k, v: fp32 [n_tokens][n_kv_heads]
+ * [head_dim] (dev, pre-RoPE keys); positions, slots: int32 [n_tokens] (dev).
+ * Slots must be distinct within one call. */
+futx_status futx_kv_append(const futx_dims* dims, int32_t n_tokens, const float* k, const float* v,
+                           const int32_t* positions, const int32_t* slots, uint32_t flags,
+                           const futx_kv_cache* cache, void* stream);
+
+/* ------------------------------------------------------------- decode block */
+
+/* Workspace bytes of futx_decode_block for up to `max_batch` sequences
+ * (1..32) of up to `max_context` cached tokens. */
+futx_status futx_decode_workspace_size(const futx_dims* dims, int32_t max_batch,
+                                       int32_t max_context, size_t* bytes);
+
+/* One decode step of one block for `batch` sequences (1..32) [ABS]:
+ *   x <- x + O(attn(rope/rotate(QKV(rmsnorm1(x)))))           (residual 1)
+ *   x <- x + DOWN(silu(GATE(rmsnorm2(x))) * UP(rmsnorm2(x)))   (residual 2)
+ * with INT4 weights dequantized into bf16 matrix-core operands and fp32
+ * accumulation [ABS, INT4].  RMSNorm gains are already folded into the QKV
+ * and GATEUP weights.  The new token's key and value are rotated, quantized
+ * and written to the cache at position cached_lens[b] (slot from the block
+ * table) before attention reads positions 0..cached_lens[b] [ABS].
+ *   x           fp32 [batch][hidden] (dev), in/out residual stream.
+ *   cached_lens int32 [batch] (dev): tokens already cached = the new token's
+ *               position.  Not modified; the caller advances it.
+ *   block_table int32 [batch][max_pages_per_seq] (dev).
+ *   workspace   >= futx_decode_workspace_size(dims, batch, max context) bytes
+ *               (dev), contents need not be initialized.
+ *   max_context upper bound on cached_lens[b] + 1 over the batch (sizes the
+ *               split-sequence attention); must be <= the workspace's. */
+futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+                              float* x, const int32_t* cached_lens, const int32_t* block_table,
+                              int32_t max_pages_per_seq, int32_t max_context,
+                              const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------ component entry points
+ * Single steps of the block, for tests and profiling. */
+
+/* out[b][n] = sum_k act[b][k] * (code[n][k] * scale[n][k / w_group]) for one
+ * packed projection: act bf16 [batch][K] (dev), out fp32 [batch][N] (dev,
+ * logical row order).  batch 1..32.  Workspace from futx_decode_workspace_size. */
+futx_status futx_int4_linear(const futx_dims* dims, futx_proj proj, const futx_qweight* w,
+                             int32_t batch, const uint16_t* act, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Decode attention alone: for query head i of sequence b, attend over cache
+ * positions 0..lens[b]-1 (note: lens counts every token to read) of KV head
+ * i / (n_heads / n_kv_heads), softmax(q k / sqrt(head_dim)) v, then the
+ * inverse block-Hadamard rotation [ABS, INT4].  q_rot: bf16 [batch][n_heads]
+ * [head_dim] rotated queries (dev); out: fp32 [batch][n_heads][head_dim]. */
+futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const uint16_t* q_rot,
+                                  const int32_t* lens, const int32_t* block_table,
+                                  int32_t max_pages_per_seq, int32_t max_context,
+                                  const futx_kv_cache* cache, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------- full decode step */
+
+/* x[b][:] = fp32(table[tokens[b]][:]) for a bf16 embedding table [vocab][hidden]. */
+futx_status futx_embed(int32_t hidden, int32_t vocab, const uint16_t* table_bf16,
+                       const int32_t* tokens, int32_t batch, float* x, void* stream);
+
+/* LM head with the final RMSNorm: logits[b][v] = (sum_k bf16(x[b][k]) w[v][k])
+ * / r_b with r_b = sqrt(mean_k x[b][k]^2 + eps), and top1[b] = the lowest
+ * index of the largest logit.  w_bf16: [vocab][hidden] with the final norm
+ * gain already folded in (see futx_fold_head).  batch 1..32. */
+futx_status futx_lm_head(const futx_dims* dims, int32_t vocab, const uint16_t* w_bf16,
+                         int32_t batch, const float* x, float* logits, int32_t* top1,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of futx_lm_head. */
+futx_status futx_lm_head_workspace_size(int32_t vocab, int32_t max_batch, size_t* bytes);
+
+/* Host-side fold of the final norm gain into the bf16 LM head:
+ * out[v][k] = bf16(fp32(w[v][k]) * gain[k]) (round to nearest even). */
+futx_status futx_fold_head(int32_t vocab, int32_t hidden, const uint16_t* w_bf16_host,
+                           const float* gain_host, uint16_t* out_bf16_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUTX_H */

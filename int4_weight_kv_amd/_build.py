@@ -1,0 +1,67 @@
+"""Builds libfutx.so (HIP for gfx950 + host C++) in the package directory.
+
+Usage: python -m int4_weight_kv_amd._build   (or __graft_entry__.build()).
+Always recompiles every source.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfutx.so")
+
+HIP_SOURCES = ["kernels.hip", "abi.hip"]
+CPP_SOURCES = ["pack.cpp"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    # packed fp32 VALU forms are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+    "-I", CSRC,
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-pthread", "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build step failed: " + " ".join(cmd))
+    return r
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in CPP_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        jobs.append([shutil.which("g++") or "g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        list(ex.map(_run, jobs))
+    objs = [j[-1] for j in jobs]
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,115 @@
+"""Device-side setup around the C ABI: packed weights, a paged INT4 KV cache
+and a workspace in torch-allocated device memory, and a thin `decode` call.
+
+Everything computational goes through libfutx.so (futx.py); torch only
+allocates memory and provides the stream.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import futx as F
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def device_buffer(nbytes, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class PackedProj:
+    packed: object  # torch uint8 device tensor
+    scales: object
+
+
+def pack_projection(dims, proj, w, gain=None, device="cuda", stream=None):
+    pb, sb = F.futx_packed_sizes(dims, proj)
+    p = device_buffer(pb, device)
+    s = device_buffer(sb, device)
+    F.futx_pack_weights(dims, proj, w, gain, p, s, stream)
+    return PackedProj(p, s)
+
+
+class DeviceLayer:
+    """One block's packed weights (device)."""
+
+    def __init__(self, dims, w, device="cuda", stream=None):
+        self.dims = dims
+        self.qkv = pack_projection(dims, "qkv", w["wqkv"], w["gain_attn"], device, stream)
+        self.o = pack_projection(dims, "o", w["wo"], None, device, stream)
+        self.gateup = pack_projection(dims, "gateup", np.concatenate([w["wgate"], w["wup"]]), w["gain_ffn"], device,
+                                      stream)
+        self.down = pack_projection(dims, "down", w["wdown"], None, device, stream)
+        self.c_weights = F.make_block_weights(*((p.packed, p.scales) for p in (self.qkv, self.o, self.gateup,
+                                                                              self.down)))
+
+    @property
+    def weight_bytes(self):
+        return sum(p.packed.numel() + p.scales.numel() for p in (self.qkv, self.o, self.gateup, self.down))
+
+
+class DeviceKVCache:
+    """A paged INT4 KV cache of one layer (device)."""
+
+    def __init__(self, dims, num_pages, device="cuda", zero=True):
+        self.dims = dims
+        self.num_pages = int(num_pages)
+        cb, sb = F.futx_kv_cache_sizes(dims, num_pages)
+        self.k_codes = device_buffer(cb, device)
+        self.v_codes = device_buffer(cb, device)
+        self.k_scales = device_buffer(sb, device)
+        self.v_scales = device_buffer(sb, device)
+        if zero:
+            for t in (self.k_codes, self.v_codes, self.k_scales, self.v_scales):
+                t.zero_()
+        self.c_cache = F.make_cache(self.k_codes, self.v_codes, self.k_scales, self.v_scales, num_pages)
+
+    def append(self, k, v, positions, slots, flags=F.FUTX_KV_ROPE | F.FUTX_KV_HADAMARD, stream=None):
+        """k, v: device fp32 [n][nkv][d]; positions, slots: device int32 [n]."""
+        F.futx_kv_append(self.dims, k.shape[0], k, v, positions, slots, flags, self.c_cache, stream)
+
+    def host_copy(self):
+        return tuple(t.cpu().numpy() for t in (self.k_codes, self.v_codes, self.k_scales, self.v_scales))
+
+
+def fill_history(cache, k_hist, v_hist, layout, b, device="cuda", stream=None, chunk=1 << 16):
+    """Writes the first len(k_hist) tokens of sequence b (positions 0..L-1)."""
+    torch = _torch()
+    L = k_hist.shape[0]
+    if L == 0:
+        return
+    for t0 in range(0, L, chunk):
+        t1 = min(L, t0 + chunk)
+        pos = np.arange(t0, t1, dtype=np.int32)
+        slots = (layout.block_table[b, pos // layout.page_size] * layout.page_size
+                 + pos % layout.page_size).astype(np.int32)
+        kd = torch.from_numpy(np.ascontiguousarray(k_hist[t0:t1])).to(device)
+        vd = torch.from_numpy(np.ascontiguousarray(v_hist[t0:t1])).to(device)
+        cache.append(kd, vd, torch.from_numpy(pos).to(device), torch.from_numpy(slots).to(device), stream=stream)
+
+
+class DecodeRunner:
+    """Workspace and metadata for futx_decode_block on one batch."""
+
+    def __init__(self, dims, batch, cached_lens, block_table, device="cuda"):
+        torch = _torch()
+        self.dims = dims
+        self.batch = int(batch)
+        self.max_context = int(np.max(cached_lens)) + 1
+        self.block_table = torch.from_numpy(np.ascontiguousarray(block_table, np.int32)).to(device)
+        self.mpps = int(block_table.shape[1])
+        self.cached_lens = torch.from_numpy(np.ascontiguousarray(cached_lens, np.int32)).to(device)
+        self.ws_bytes = F.futx_decode_workspace_size(dims, self.batch, self.max_context)
+        self.workspace = device_buffer(self.ws_bytes, device)
+
+    def decode(self, layer, cache, x, stream=None):
+        """x: device fp32 [B][hidden], updated in place."""
+        F.futx_decode_block(self.dims, layer.c_weights, self.batch, x, self.cached_lens, self.block_table,
+                            self.mpps, self.max_context, cache.c_cache, self.workspace, self.ws_bytes, stream)

@@ -1,0 +1,398 @@
+// C-ABI entry points of libfutx.so (declared in include/futx.h): argument
+// validation, workspace carving and the launch order of the decode block.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+#include "kernels.h"
+
+namespace futx {
+
+futx_status pack_host(const futx_dims* dims, futx_proj proj, const float* w, const float* gain,
+                      void* packed, void* scales);
+futx_status unpack_host(const futx_dims* dims, futx_proj proj, const void* packed,
+                        const void* scales, uint8_t* canon, uint16_t* canon_scales);
+futx_status fold_head_host(int32_t vocab, int32_t hidden, const uint16_t* w, const float* gain,
+                           uint16_t* out);
+
+static thread_local char g_err[512];
+
+futx_status fail(futx_status status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+static futx_status hip_fail(hipError_t e, const char* what) {
+  return fail(FUTX_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FUTX_HIP(call, what)                      \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+static bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+futx_status check_dims(const futx_dims* d) {
+  if (!d) return fail(FUTX_E_ARG, "dims is NULL");
+  if (d->hidden <= 0 || d->n_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->intermediate <= 0 || d->w_group <= 0 || d->had_block <= 0 || d->page_size <= 0)
+    return fail(FUTX_E_ARG, "dims: every size must be positive");
+  if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f)) return fail(FUTX_E_ARG, "dims: bad eps or theta");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(FUTX_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->w_group != 64 && d->w_group != 128) return fail(FUTX_E_UNSUPPORTED, "w_group must be 64 or 128");
+  if (!pow2(d->had_block) || d->had_block > 64 || d->had_block < 2 || d->head_dim % d->had_block)
+    return fail(FUTX_E_UNSUPPORTED, "had_block must be a power of two <= 64 dividing head_dim");
+  if (d->page_size != kPageSize) return fail(FUTX_E_UNSUPPORTED, "page_size must be 64");
+  if (d->n_heads % d->n_kv_heads || d->n_heads / d->n_kv_heads > 16)
+    return fail(FUTX_E_UNSUPPORTED, "n_heads must be a multiple of n_kv_heads with at most 16 per group");
+  if (d->head_dim % d->w_group) return fail(FUTX_E_UNSUPPORTED, "head_dim must be a multiple of w_group");
+  const int ks[3] = {d->hidden, d->n_heads * d->head_dim, d->intermediate};
+  for (int k : ks)
+    if (k % kTileK || k % d->w_group) return fail(FUTX_E_UNSUPPORTED, "projection inputs must be multiples of 128");
+  if (d->hidden % kTileN || d->intermediate % kTileN) return fail(FUTX_E_UNSUPPORTED, "bad row count");
+  return FUTX_OK;
+}
+
+futx_status check_proj(futx_proj p) {
+  if (p < FUTX_PROJ_QKV || p > FUTX_PROJ_DOWN) return fail(FUTX_E_ARG, "unknown projection %d", (int)p);
+  return FUTX_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+
+struct Ws {
+  uint16_t* act;   // [32][Kmax] bf16
+  float* gsum;     // [Kmax / G][32]
+  float* invr;     // [32]
+  float* invr2;    // [32]
+  float* part;     // split-K partials
+  float* qkv;      // [B][Nqkv]
+  float* qrot;     // [B][nq][D] rotated queries
+  float* apart;    // [B][nq][nsplit][D + 2]
+  float* h;        // [B][H]
+  size_t bytes;
+};
+
+static int kmax(const futx_dims& d) {
+  int k = d.hidden;
+  if (d.n_heads * d.head_dim > k) k = d.n_heads * d.head_dim;
+  if (d.intermediate > k) k = d.intermediate;
+  return k;
+}
+
+static size_t part_floats(const futx_dims& d, int B) {
+  size_t m = 0;
+  for (int p = 0; p < 4; ++p) {
+    ProjShape s = proj_shape(d, (futx_proj)p);
+    GemmPlan g = gemm_plan(s.n, s.k);
+    size_t v = (size_t)g.splits * B * s.n;
+    if (v > m) m = v;
+  }
+  return m;
+}
+
+static Ws carve(const futx_dims& d, int B, int max_ctx, char* base) {
+  Ws w{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + at : nullptr;
+    at += round_up(bytes, 256);
+    return p;
+  };
+  const int K = kmax(d);
+  const int D = d.head_dim, nq = d.n_heads;
+  const int nqkv = (d.n_heads + 2 * d.n_kv_heads) * D;
+  const int nsplit = (max_ctx + kPageSize - 1) / kPageSize;  // chunk >= one page
+  w.act = (uint16_t*)take((size_t)kMaxBatch * K * 2);
+  w.gsum = (float*)take((size_t)(K / d.w_group) * kMaxBatch * 4);
+  w.invr = (float*)take(kMaxBatch * 4);
+  w.invr2 = (float*)take(kMaxBatch * 4);
+  w.part = (float*)take(part_floats(d, B) * 4);
+  w.qkv = (float*)take((size_t)B * nqkv * 4);
+  w.qrot = (float*)take((size_t)B * nq * D * 4);
+  w.apart = (float*)take((size_t)B * nq * (nsplit < 1 ? 1 : nsplit) * (D + 2) * 4);
+  w.h = (float*)take((size_t)B * d.hidden * 4);
+  w.bytes = at;
+  return w;
+}
+
+static KVPtrs kv_ptrs(const futx_kv_cache* c, int nkv) {
+  return KVPtrs{(uint8_t*)c->k_codes, (uint8_t*)c->v_codes, (uint16_t*)c->k_scales,
+                (uint16_t*)c->v_scales, nkv};
+}
+
+static KVPtrsConst kv_cptrs(const futx_kv_cache* c, int nkv) {
+  return KVPtrsConst{(const uint8_t*)c->k_codes, (const uint8_t*)c->v_codes,
+                     (const uint16_t*)c->k_scales, (const uint16_t*)c->v_scales, nkv};
+}
+
+static futx_status check_cache(const futx_kv_cache* c) {
+  if (!c || !c->k_codes || !c->v_codes || !c->k_scales || !c->v_scales || c->num_pages <= 0)
+    return fail(FUTX_E_ARG, "kv cache: null pointer or no pages");
+  return FUTX_OK;
+}
+
+static futx_status check_qweight(const futx_qweight* q, const char* name) {
+  if (!q || !q->packed || !q->scales) return fail(FUTX_E_ARG, "weights %s: null pointer", name);
+  if (((uintptr_t)q->packed | (uintptr_t)q->scales) & 15)
+    return fail(FUTX_E_ARG, "weights %s: buffers must be 16-byte aligned", name);
+  return FUTX_OK;
+}
+
+}  // namespace futx
+
+using namespace futx;
+
+extern "C" {
+
+const char* futx_last_error(void) { return g_err; }
+
+futx_status futx_packed_sizes(const futx_dims* dims, futx_proj proj, size_t* packed_bytes,
+                              size_t* scale_bytes) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st || (st = check_proj(proj))) return st;
+  if (!packed_bytes || !scale_bytes) return fail(FUTX_E_ARG, "null output pointer");
+  ProjShape s = proj_shape(*dims, proj);
+  *packed_bytes = (size_t)s.n * s.k / 2;
+  *scale_bytes = (size_t)s.n * (s.k / dims->w_group) * 2;
+  return FUTX_OK;
+}
+
+futx_status futx_pack_weights_host(const futx_dims* dims, futx_proj proj, const float* w_host,
+                                   const float* gain_host, void* packed_host, void* scales_host) {
+  clear_error();
+  return pack_host(dims, proj, w_host, gain_host, packed_host, scales_host);
+}
+
+futx_status futx_pack_weights(const futx_dims* dims, futx_proj proj, const float* w_host,
+                              const float* gain_host, void* packed_dev, void* scales_dev,
+                              void* stream) {
+  clear_error();
+  size_t pb, sb;
+  futx_status st = futx_packed_sizes(dims, proj, &pb, &sb);
+  if (st) return st;
+  if (!packed_dev || !scales_dev) return fail(FUTX_E_ARG, "pack: null device pointer");
+  std::vector<uint8_t> hp(pb);
+  std::vector<uint8_t> hs(sb);
+  st = pack_host(dims, proj, w_host, gain_host, hp.data(), hs.data());
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  FUTX_HIP(hipMemcpyAsync(packed_dev, hp.data(), pb, hipMemcpyHostToDevice, s), "pack: copy");
+  FUTX_HIP(hipMemcpyAsync(scales_dev, hs.data(), sb, hipMemcpyHostToDevice, s), "pack: copy");
+  FUTX_HIP(hipStreamSynchronize(s), "pack: sync");
+  return FUTX_OK;
+}
+
+futx_status futx_unpack_weights(const futx_dims* dims, futx_proj proj, const void* packed_dev,
+                                const void* scales_dev, uint8_t* canon_bytes_host,
+                                uint16_t* canon_scales_host, void* stream) {
+  clear_error();
+  size_t pb, sb;
+  futx_status st = futx_packed_sizes(dims, proj, &pb, &sb);
+  if (st) return st;
+  if (!packed_dev || !scales_dev || !canon_bytes_host || !canon_scales_host)
+    return fail(FUTX_E_ARG, "unpack: null pointer");
+  std::vector<uint8_t> hp(pb), hs(sb);
+  hipStream_t s = (hipStream_t)stream;
+  FUTX_HIP(hipMemcpyAsync(hp.data(), packed_dev, pb, hipMemcpyDeviceToHost, s), "unpack: copy");
+  FUTX_HIP(hipMemcpyAsync(hs.data(), scales_dev, sb, hipMemcpyDeviceToHost, s), "unpack: copy");
+  FUTX_HIP(hipStreamSynchronize(s), "unpack: sync");
+  return unpack_host(dims, proj, hp.data(), hs.data(), canon_bytes_host, canon_scales_host);
+}
+
+futx_status futx_kv_cache_sizes(const futx_dims* dims, int32_t num_pages, size_t* code_bytes,
+                                size_t* scale_bytes) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st) return st;
+  if (num_pages <= 0 || !code_bytes || !scale_bytes) return fail(FUTX_E_ARG, "kv sizes: bad args");
+  *code_bytes = (size_t)num_pages * dims->n_kv_heads * kPageSize * dims->head_dim / 2;
+  *scale_bytes = (size_t)num_pages * dims->n_kv_heads * kPageSize * 2;
+  return FUTX_OK;
+}
+
+futx_status futx_kv_append(const futx_dims* dims, int32_t n_tokens, const float* k, const float* v,
+                           const int32_t* positions, const int32_t* slots, uint32_t flags,
+                           const futx_kv_cache* cache, void* stream) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st || (st = check_cache(cache))) return st;
+  if (n_tokens < 0) return fail(FUTX_E_ARG, "kv_append: negative token count");
+  if (n_tokens == 0) return FUTX_OK;
+  if (!k || !v || !slots || ((flags & FUTX_KV_ROPE) && !positions))
+    return fail(FUTX_E_ARG, "kv_append: null pointer");
+  if (flags & ~(FUTX_KV_ROPE | FUTX_KV_HADAMARD)) return fail(FUTX_E_ARG, "kv_append: unknown flags");
+  hipError_t e = launch_kv_append(k, v, positions, slots, n_tokens, flags, dims->head_dim,
+                                  dims->had_block, dims->rope_theta,
+                                  kv_ptrs(cache, dims->n_kv_heads), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_append: launch");
+  return FUTX_OK;
+}
+
+futx_status futx_decode_workspace_size(const futx_dims* dims, int32_t max_batch,
+                                       int32_t max_context, size_t* bytes) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st) return st;
+  if (max_batch < 1 || max_batch > kMaxBatch || max_context < 1 || !bytes)
+    return fail(FUTX_E_ARG, "workspace size: batch must be 1..32 and context >= 1");
+  *bytes = carve(*dims, max_batch, max_context, nullptr).bytes;
+  return FUTX_OK;
+}
+
+futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+                              float* x, const int32_t* cached_lens, const int32_t* block_table,
+                              int32_t max_pages_per_seq, int32_t max_context,
+                              const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st || (st = check_cache(cache))) return st;
+  if (!w) return fail(FUTX_E_ARG, "decode_block: weights is NULL");
+  if ((st = check_qweight(&w->qkv, "qkv")) || (st = check_qweight(&w->o, "o")) ||
+      (st = check_qweight(&w->gateup, "gateup")) || (st = check_qweight(&w->down, "down")))
+    return st;
+  if (batch < 1 || batch > kMaxBatch) return fail(FUTX_E_ARG, "decode_block: batch must be 1..32");
+  if (!x || !cached_lens || !block_table || !workspace)
+    return fail(FUTX_E_ARG, "decode_block: null pointer");
+  if (max_pages_per_seq < 1 || max_context < 1 ||
+      (long)max_pages_per_seq * kPageSize < (long)max_context)
+    return fail(FUTX_E_ARG, "decode_block: max_context exceeds the block table");
+  const futx_dims& d = *dims;
+  Ws ws = carve(d, batch, max_context, (char*)workspace);
+  if (ws.bytes > workspace_bytes)
+    return fail(FUTX_E_WORKSPACE, "decode_block: workspace %zu < %zu bytes", workspace_bytes, ws.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const int B = batch, H = d.hidden, D = d.head_dim, nq = d.n_heads, G = d.w_group;
+  const int nqkv = (d.n_heads + 2 * d.n_kv_heads) * D, I = d.intermediate;
+  const KVPtrs kv = kv_ptrs(cache, d.n_kv_heads);
+  const KVPtrsConst kvc = kv_cptrs(cache, d.n_kv_heads);
+  hipError_t e;
+#define STEP(call)                                             \
+  do {                                                         \
+    if ((e = (call)) != hipSuccess) return hip_fail(e, #call); \
+  } while (0)
+  // RMSNorm-1 operand and 1/r
+  STEP(launch_prep_act(x, B, H, d.rms_eps, ws.act, ws.invr, s));
+  STEP(launch_gsum(ws.act, B, H, G, ws.gsum, s));
+  // QKV
+  GemmPlan gq = gemm_plan(nqkv, H);
+  STEP(launch_gemm_partial(w->qkv.packed, w->qkv.scales, ws.act, ws.gsum, B, nqkv, H, G, ws.part, gq, s));
+  STEP(launch_reduce(ws.part, gq.splits, B, nqkv, ws.invr, nullptr, ws.qkv, 0, s));
+  // RoPE, rotation, INT4 append of the new token; rotated bf16 queries
+  STEP(launch_post_qkv(ws.qkv, B, nq, D, cached_lens, block_table, max_pages_per_seq, d.had_block,
+                       d.rope_theta, ws.qrot, kv, s));
+  // attention over positions 0..cached_lens[b]
+  AttnPlan ap = attn_plan(B, d.n_kv_heads, max_context);
+  STEP(launch_attention(ws.qrot, true, cached_lens, 1, block_table, max_pages_per_seq, B, nq, D,
+                        ap, kvc, ws.apart, s));
+  STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act,
+                         ws.gsum, G, s));
+  // O projection + residual
+  GemmPlan go = gemm_plan(H, nq * D);
+  STEP(launch_gemm_partial(w->o.packed, w->o.scales, ws.act, ws.gsum, B, H, nq * D, G, ws.part, go, s));
+  STEP(launch_reduce(ws.part, go.splits, B, H, nullptr, x, ws.h, 0, s));
+  // RMSNorm-2 operand, gate/up + SwiGLU
+  STEP(launch_prep_act(ws.h, B, H, d.rms_eps, ws.act, ws.invr2, s));
+  STEP(launch_gsum(ws.act, B, H, G, ws.gsum, s));
+  GemmPlan gg = gemm_plan(2 * I, H);
+  STEP(launch_gemm_partial(w->gateup.packed, w->gateup.scales, ws.act, ws.gsum, B, 2 * I, H, G, ws.part, gg, s));
+  STEP(launch_swiglu(ws.part, gg.splits, B, I, G, ws.invr2, ws.act, ws.gsum, s));
+  // down projection + residual
+  GemmPlan gd = gemm_plan(H, I);
+  STEP(launch_gemm_partial(w->down.packed, w->down.scales, ws.act, ws.gsum, B, H, I, G, ws.part, gd, s));
+  STEP(launch_reduce(ws.part, gd.splits, B, H, nullptr, ws.h, x, 0, s));
+#undef STEP
+  return FUTX_OK;
+}
+
+futx_status futx_int4_linear(const futx_dims* dims, futx_proj proj, const futx_qweight* w,
+                             int32_t batch, const uint16_t* act, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st || (st = check_proj(proj)) || (st = check_qweight(w, "linear"))) return st;
+  if (batch < 1 || batch > kMaxBatch || !act || !out || !workspace)
+    return fail(FUTX_E_ARG, "int4_linear: bad args");
+  Ws ws = carve(*dims, batch, 1, (char*)workspace);
+  if (ws.bytes > workspace_bytes)
+    return fail(FUTX_E_WORKSPACE, "int4_linear: workspace %zu < %zu bytes", workspace_bytes, ws.bytes);
+  ProjShape ps = proj_shape(*dims, proj);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  GemmPlan g = gemm_plan(ps.n, ps.k);
+  if ((e = launch_gsum(act, batch, ps.k, dims->w_group, ws.gsum, s)) != hipSuccess) return hip_fail(e, "gsum");
+  if ((e = launch_gemm_partial(w->packed, w->scales, act, ws.gsum, batch, ps.n, ps.k, dims->w_group,
+                               ws.part, g, s)) != hipSuccess)
+    return hip_fail(e, "gemm");
+  if ((e = launch_reduce(ws.part, g.splits, batch, ps.n, nullptr, nullptr, out,
+                         proj == FUTX_PROJ_GATEUP ? dims->intermediate : 0, s)) != hipSuccess)
+    return hip_fail(e, "reduce");
+  return FUTX_OK;
+}
+
+futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const uint16_t* q_rot,
+                                  const int32_t* lens, const int32_t* block_table,
+                                  int32_t max_pages_per_seq, int32_t max_context,
+                                  const futx_kv_cache* cache, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st || (st = check_cache(cache))) return st;
+  if (batch < 1 || batch > kMaxBatch || !q_rot || !lens || !block_table || !out || !workspace)
+    return fail(FUTX_E_ARG, "decode_attention: bad args");
+  if (max_pages_per_seq < 1 || max_context < 1 ||
+      (long)max_pages_per_seq * kPageSize < (long)max_context)
+    return fail(FUTX_E_ARG, "decode_attention: max_context exceeds the block table");
+  const futx_dims& d = *dims;
+  Ws ws = carve(d, batch, max_context, (char*)workspace);
+  if (ws.bytes > workspace_bytes)
+    return fail(FUTX_E_WORKSPACE, "decode_attention: workspace %zu < %zu bytes", workspace_bytes, ws.bytes);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  AttnPlan ap = attn_plan(batch, d.n_kv_heads, max_context);
+  if ((e = launch_attention(q_rot, false, lens, 0, block_table, max_pages_per_seq, batch, d.n_heads,
+                            d.head_dim, ap, kv_cptrs(cache, d.n_kv_heads), ws.apart, s)) != hipSuccess)
+    return hip_fail(e, "attention");
+  if ((e = launch_attn_merge(ws.apart, lens, 0, batch, d.n_heads, d.head_dim, ap, d.had_block, out,
+                             nullptr, nullptr, d.w_group, s)) != hipSuccess)
+    return hip_fail(e, "merge");
+  return FUTX_OK;
+}
+
+futx_status futx_embed(int32_t hidden, int32_t vocab, const uint16_t* table_bf16,
+                       const int32_t* tokens, int32_t batch, float* x, void* stream) {
+  clear_error();
+  return fail(FUTX_E_UNSUPPORTED, "embed: not built yet");
+}
+
+futx_status futx_lm_head(const futx_dims* dims, int32_t vocab, const uint16_t* w_bf16,
+                         int32_t batch, const float* x, float* logits, int32_t* top1,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return fail(FUTX_E_UNSUPPORTED, "lm_head: not built yet");
+}
+
+futx_status futx_lm_head_workspace_size(int32_t vocab, int32_t max_batch, size_t* bytes) {
+  clear_error();
+  return fail(FUTX_E_UNSUPPORTED, "lm_head: not built yet");
+}
+
+futx_status futx_fold_head(int32_t vocab, int32_t hidden, const uint16_t* w_bf16_host,
+                           const float* gain_host, uint16_t* out_bf16_host) {
+  clear_error();
+  return fold_head_host(vocab, hidden, w_bf16_host, gain_host, out_bf16_host);
+}
+
+}  // extern "C"

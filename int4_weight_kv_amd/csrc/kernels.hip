@@ -1,0 +1,728 @@
+// gfx950 kernels of the INT4 decode block (multi-kernel path).
+//
+// Each kernel implements one step of the decode block described in the
+// FuTransformer abstract (airebao.com item page) and the kongchang.com/en
+// article, section "INT4 Decode: letting dequantization feed directly into
+// MMA operands": INT4 projections whose nibbles are widened to bf16 in
+// registers and fed to the matrix cores, a rotated INT4 KV cache, and
+// split-sequence decode attention.  Operand and cache layouts: layout.h.
+#include "device.h"
+#include "futx.h"
+#include "kernels.h"
+
+namespace futx {
+
+// ---------------------------------------------------------------- activations
+
+// act[b][:] = bf16(x[b][:]); invr[b] = 1 / sqrt(mean(x[b]^2) + eps).
+// RMSNorm reading: the gain lives in the next weights and 1/r is applied to
+// the GEMM result, so the matrix-core operand is bf16(x).
+__global__ __launch_bounds__(256) void prep_act_kernel(const float* __restrict__ x, int H, float eps,
+                                                       uint16_t* __restrict__ act,
+                                                       float* __restrict__ invr) {
+  const int b = blockIdx.x;
+  const float* xr = x + (size_t)b * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += 256) {
+    float v = xr[c];
+    ss += v * v;
+    act[(size_t)b * H + c] = f32_to_bf16_bits(v);
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) invr[b] = 1.0f / sqrtf(red[0] / (float)H + eps);
+}
+
+// gsum[j * 32 + b] = sum of the bf16 values act[b][j*G .. j*G+G-1] (fp32).
+__global__ __launch_bounds__(64) void gsum_kernel(const uint16_t* __restrict__ act, int K, int G,
+                                                  float* __restrict__ gsum) {
+  const int j = blockIdx.x, b = blockIdx.y;
+  float s = 0.f;
+  for (int c = threadIdx.x; c < G; c += 64) s += bf16_bits_to_f32(act[(size_t)b * K + (size_t)j * G + c]);
+  s = wave_sum(s);
+  if (threadIdx.x == 0) gsum[j * kMaxBatch + b] = s;
+}
+
+// ---------------------------------------------------------------- INT4 GEMM
+
+// Split-K partial products of one packed projection.  One wave per
+// (16-row tile, K split); per K block it loads 16 bytes of nibbles per lane
+// (four MFMA steps), widens them to bf16 in registers and multiplies with
+// the bf16 activations.  Per weight group the MFMA sum is corrected for the
+// nibble offset with the activation group sum and scaled by the group scale.
+// part[split][b][P] (fp32, physical row order).
+template <int G, int NF>
+__global__ __launch_bounds__(256) void gemm_partial_kernel(
+    const uint4* __restrict__ wpk, const uint16_t* __restrict__ wsc,
+    const uint16_t* __restrict__ act, const float* __restrict__ gsum, int B, int N, int K,
+    int kbps, int S, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ntiles = N / 16;
+  if (wid >= ntiles * S) return;
+  const int nt = wid / S, split = wid - nt * S;
+  const int KB = K / 128;
+  const int kb0 = split * kbps, kb1 = min(kb0 + kbps, KB);
+  const int col = lane & 15, grp = lane >> 4;
+  const int n = nt * 16 + col;
+  const int ngroups = K / G;
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const uint4 wv = wpk[((size_t)nt * KB + kb) * 64 + lane];
+    bf16x8 a[NF][4];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int tok = f * 16 + col;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 av = {0u, 0u, 0u, 0u};
+        if (tok < B) av = *(const uint4*)(act + (size_t)tok * K + kb * 128 + s * 32 + grp * 8);
+        a[f][s] = as_bf16x8(av);
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < 128 / G; ++gi) {
+      f32x4 d[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) d[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ss = 0; ss < G / 32; ++ss) {
+        const int s = gi * (G / 32) + ss;
+        const bf16x8 bw = widen_word(word_of(wv, s));
+#pragma unroll
+        for (int f = 0; f < NF; ++f) d[f] = mfma16(a[f][s], bw, d[f]);
+      }
+      const int j = kb * (128 / G) + gi;
+      const float sc = half_bits_to_f32(wsc[(size_t)n * ngroups + j]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = f * 16 + 4 * grp + r;
+          const float gs = tok < B ? gsum[j * kMaxBatch + tok] : 0.f;
+          acc[f][r] += sc * (d[f][r] - kBias * gs);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = f * 16 + 4 * grp + r;
+      if (tok < B) part[((size_t)split * B + tok) * N + n] = acc[f][r];
+    }
+  }
+}
+
+__device__ __forceinline__ int physical_row(int n, int gateup_inter) {
+  if (!gateup_inter) return n;
+  const int half = n / gateup_inter, r = n - half * gateup_inter;
+  return (2 * (r >> 4) + half) * 16 + (r & 15);
+}
+
+// out[b][n] = resid[b][n] + rowscale[b] * sum_s part[s][b][P(n)]  (n logical)
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int S, int B,
+                                                     int N, const float* __restrict__ rowscale,
+                                                     const float* resid, float* out,
+                                                     int gateup_inter) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= B * N) return;
+  const int b = idx / N, n = idx - b * N;
+  const int P = physical_row(n, gateup_inter);
+  float s = 0.f;
+  for (int sp = 0; sp < S; ++sp) s += part[((size_t)sp * B + b) * N + P];
+  if (rowscale) s *= rowscale[b];
+  if (resid) s += resid[idx];
+  out[idx] = s;
+}
+
+// SwiGLU of the gate/up partials: act[b][c] = bf16(silu(g) * u) with
+// g = invr[b] * sum(gate partials), u = invr[b] * sum(up partials); also the
+// bf16 group sums of act for the down projection.  One block of G threads
+// per (group, sequence).
+__global__ __launch_bounds__(128) void swiglu_kernel(const float* __restrict__ part, int S, int B,
+                                                     int I, int G, const float* __restrict__ invr,
+                                                     uint16_t* __restrict__ act,
+                                                     float* __restrict__ gsum) {
+  const int c = blockIdx.x * G + threadIdx.x, b = blockIdx.y;
+  const int N = 2 * I;
+  const int Pg = 32 * (c >> 4) + (c & 15), Pu = Pg + 16;
+  float g = 0.f, u = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    g += part[((size_t)sp * B + b) * N + Pg];
+    u += part[((size_t)sp * B + b) * N + Pu];
+  }
+  g *= invr[b];
+  u *= invr[b];
+  const float a = g / (1.0f + expf(-g)) * u;
+  const uint16_t ab = f32_to_bf16_bits(a);
+  act[(size_t)b * I + c] = ab;
+  float s = wave_sum(bf16_bits_to_f32(ab));
+  __shared__ float red[2];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) gsum[blockIdx.x * kMaxBatch + b] = G > 64 ? red[0] + red[1] : red[0];
+}
+
+// ---------------------------------------------------------------- KV append
+
+// cos / sin of the RoPE angle pos * theta^(-2i/d), computed in fp64 so that
+// long positions keep full fp32 accuracy.
+__device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float* c, float* s) {
+  const double inv = pow((double)theta, -2.0 * (double)i / (double)d);
+  const double ang = (double)pos * inv;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// Rotate-half RoPE of one head held as channel c = lane + 64 j.
+template <int D>
+__device__ __forceinline__ void rope_lane(float (&x)[D / 64], int pos, float theta) {
+  const int lane = threadIdx.x & 63;
+  float c, s;
+  if constexpr (D == 128) {
+    rope_cs(pos, lane, D, theta, &c, &s);
+    const float a = x[0], b = x[1];
+    x[0] = a * c - b * s;
+    x[1] = b * c + a * s;
+  } else {
+    rope_cs(pos, lane & 31, D, theta, &c, &s);
+    const float o = __shfl_xor(x[0], 32, 64);
+    x[0] = lane < 32 ? x[0] * c - o * s : x[0] * c + o * s;
+  }
+}
+
+// Normalized Sylvester Hadamard over contiguous blocks of hb channels
+// (hb divides 64, so a block never leaves its 64-lane row).
+template <int D>
+__device__ __forceinline__ void fwht_lane(float (&x)[D / 64], int hb) {
+  const int lane = threadIdx.x & 63;
+  for (int hop = 1; hop < hb; hop <<= 1) {
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      const float o = __shfl_xor(x[j], hop, 64);
+      x[j] = (lane & hop) ? o - x[j] : x[j] + o;
+    }
+  }
+  const float sc = 1.0f / sqrtf((float)hb);
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) x[j] *= sc;
+}
+
+// Per-(token, head) INT4 quantization (fp32 recipe, scale saturated at the
+// fp16 maximum).  Returns the fp16 scale bits; codes in q[].
+template <int D>
+__device__ __forceinline__ uint16_t quantize_lane(const float (&x)[D / 64], int (&q)[D / 64]) {
+  float am = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) am = fmaxf(am, fabsf(x[j]));
+  am = wave_max(am);
+  const float s32 = fminf(am / 7.0f, 65504.0f);
+  const __half s16 = __float2half_rn(s32);
+  const float sf = __half2float(s16);
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    float v = sf == 0.f ? 0.f : rintf(x[j] / sf);
+    q[j] = (int)fminf(fmaxf(v, -8.f), 7.f);
+  }
+  return __half_as_ushort(s16);
+}
+
+__device__ __forceinline__ int nibble_bit(int e) { return (e & 1) ? 16 + 4 * (e >> 1) : 4 * (e >> 1); }
+
+// Writes one rotated token of KV head h into its slot.
+template <int D>
+__device__ void store_token(const float (&kx)[D / 64], const float (&vx)[D / 64], int slot, int h,
+                            const KVPtrs& kv) {
+  const int lane = threadIdx.x & 63;
+  const int page = slot / kPageSize, off = slot % kPageSize;
+  const size_t head_base = ((size_t)page * kv.nkv + h) * (size_t)(kPageSize * D / 2);
+  int qk[D / 64], qv[D / 64];
+  const uint16_t sk = quantize_lane<D>(kx, qk);
+  const uint16_t sv = quantize_lane<D>(vx, qv);
+  // keys: 8 consecutive channels form one word of the lane chunk of token off
+  const int e = lane & 7, g = (lane & 31) >> 3;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    uint32_t w = (uint32_t)(qk[j] + (int)kNibbleBias) << nibble_bit(e);
+    w |= __shfl_xor(w, 1, 64);
+    w |= __shfl_xor(w, 2, 64);
+    w |= __shfl_xor(w, 4, 64);
+    if (e == 0) {
+      const int s = (lane >> 5) + 2 * j;
+      uint8_t* p = kv.k_codes + head_base + (size_t)(off >> 4) * (8 * D) +
+                   (size_t)(g * 16 + (off & 15)) * (D / 8) + s * 4;
+      *(uint32_t*)p = w;
+    }
+  }
+  // values: one nibble per channel in a word shared with 7 other tokens
+  const int tb = off >> 5, tp = off & 31;
+  const int gv = tp < 16 ? tp >> 2 : (tp - 16) >> 2;
+  const int ev = tp < 16 ? (tp & 3) : 4 + ((tp - 16) & 3);
+  const int bit = nibble_bit(ev);
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    const int c = lane + 64 * j;
+    const int cg = c >> 6, c4 = (c & 63) >> 4;
+    uint32_t* p = (uint32_t*)(kv.v_codes + head_base + (size_t)(tb * (D / 64) + cg) * 1024 +
+                              (size_t)(gv * 16 + (c & 15)) * 16 + c4 * 4);
+    atomicAnd(p, ~(0xFu << bit));
+    atomicOr(p, (uint32_t)(qv[j] + (int)kNibbleBias) << bit);
+  }
+  if (lane == 0) {
+    kv.k_scales[((size_t)page * kv.nkv + h) * kPageSize + off] = sk;
+    kv.v_scales[((size_t)page * kv.nkv + h) * kPageSize + off] = sv;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void kv_append_kernel(const float* __restrict__ k,
+                                                       const float* __restrict__ v,
+                                                       const int32_t* __restrict__ positions,
+                                                       const int32_t* __restrict__ slots,
+                                                       uint32_t flags, int hb, float theta,
+                                                       KVPtrs kv) {
+  const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const size_t base = ((size_t)t * kv.nkv + h) * D;
+  float kx[D / 64], vx[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    kx[j] = k[base + lane + 64 * j];
+    vx[j] = v[base + lane + 64 * j];
+  }
+  if (flags & FUTX_KV_ROPE) rope_lane<D>(kx, positions[t], theta);
+  if (flags & FUTX_KV_HADAMARD) {
+    fwht_lane<D>(kx, hb);
+    fwht_lane<D>(vx, hb);
+  }
+  store_token<D>(kx, vx, slots[t], h, kv);
+}
+
+// After the QKV projection: RoPE + rotation of the queries (fp32 q_rot), and
+// RoPE + rotation + INT4 append of the new key and value.
+template <int D>
+__global__ __launch_bounds__(64) void post_qkv_kernel(const float* __restrict__ qkv, int nq,
+                                                      const int32_t* __restrict__ cached_lens,
+                                                      const int32_t* __restrict__ block_table,
+                                                      int mpps, int hb, float theta,
+                                                      float* __restrict__ qrot, KVPtrs kv) {
+  const int hh = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int nkv = kv.nkv;
+  const int nqkv = (nq + 2 * nkv) * D;
+  const int pos = cached_lens[b];
+  const float* row = qkv + (size_t)b * nqkv;
+  if (hh < nq) {
+    float x[D / 64];
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) x[j] = row[hh * D + lane + 64 * j];
+    rope_lane<D>(x, pos, theta);
+    fwht_lane<D>(x, hb);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) qrot[((size_t)b * nq + hh) * D + lane + 64 * j] = x[j];
+  } else {
+    const int h = hh - nq;
+    float kx[D / 64], vx[D / 64];
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      kx[j] = row[(nq + h) * D + lane + 64 * j];
+      vx[j] = row[(nq + nkv + h) * D + lane + 64 * j];
+    }
+    rope_lane<D>(kx, pos, theta);
+    fwht_lane<D>(kx, hb);
+    fwht_lane<D>(vx, hb);
+    const int slot = block_table[(size_t)b * mpps + pos / kPageSize] * kPageSize + pos % kPageSize;
+    store_token<D>(kx, vx, slot, h, kv);
+  }
+}
+
+// ---------------------------------------------------------------- attention
+
+// Split-sequence decode attention.  One wave per (chunk, KV head, sequence)
+// computes, for the G query heads of the KV head, the chunk's running max m,
+// normalizer l and unnormalized p.v accumulator over rotated INT4 keys and
+// values (flash-decoding partials, merged by attn_merge_kernel).
+//   q.k:  A = key tile (16 tokens x 32 channels per MFMA), B = rotated query
+//         (query heads as columns) -> scores[token][head] with the token of
+//         lane L, reg r at 4 (L/16) + r.
+//   p.v:  A = probabilities (heads x 32 tokens) built directly from the two
+//         score tiles of a 32-token block, B = value tile.
+// Both fp32 operands (the query and p * value scale) enter the bf16 MFMA as
+// a hi + lo pair of bf16 values, so the products keep about 16 significant
+// bits instead of 8.  Nibble offsets are removed with the operand sums.
+// apart[((b * nq + i) * nsplit + sp) * (D + 2)] = {m, l, acc[0..D)}.
+__device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo) {
+  *hi = f32_to_bf16_bits(x);
+  *lo = f32_to_bf16_bits(x - bf16_bits_to_f32(*hi));
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+
+template <int D, bool QF32>
+__global__ __launch_bounds__(64) void attn_split_kernel(
+    const void* __restrict__ qin, const int32_t* __restrict__ lens, int len_add,
+    const int32_t* __restrict__ block_table, int mpps, int nq, int chunk, int nsplit, float scale,
+    KVPtrsConst kv, float* __restrict__ apart) {
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int nkv = kv.nkv, G = nq / nkv;
+  const int L = lens[b] + len_add;
+  const int t0 = sp * chunk, t1 = min(t0 + chunk, L);
+  if (t0 >= t1) return;
+  const int col = lane & 15, grp = lane >> 4;
+  // query fragments (B operand): column = query head h*G + col
+  bf16x8 qh[D / 32], ql[D / 32];
+  float qs = 0.f;
+  {
+    const bool ok = col < G;
+    const size_t qoff = ((size_t)b * nq + h * G + col) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      uint32_t hw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+      if (ok) {
+        if constexpr (QF32) {
+          const float4* qp = (const float4*)((const float*)qin + qoff + s * 32 + grp * 8);
+          const float4 a = qp[0], c = qp[1];
+          const float f[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            uint16_t h0, l0, h1, l1;
+            split_bf16(f[e], &h0, &l0);
+            split_bf16(f[e + 1], &h1, &l1);
+            hw[e / 2] = pack2(h0, h1);
+            lw[e / 2] = pack2(l0, l1);
+            qs += (bf16_bits_to_f32(h0) + bf16_bits_to_f32(l0)) + (bf16_bits_to_f32(h1) + bf16_bits_to_f32(l1));
+          }
+        } else {
+          const uint4 v = *(const uint4*)((const uint16_t*)qin + qoff + s * 32 + grp * 8);
+          hw[0] = v.x; hw[1] = v.y; hw[2] = v.z; hw[3] = v.w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            qs += bf16_bits_to_f32(hw[e] & 0xFFFF) + bf16_bits_to_f32(hw[e] >> 16);
+        }
+      }
+      qh[s] = as_bf16x8(uint4{hw[0], hw[1], hw[2], hw[3]});
+      ql[s] = as_bf16x8(uint4{lw[0], lw[1], lw[2], lw[3]});
+    }
+  }
+  qs += __shfl_xor(qs, 16, 64);
+  qs += __shfl_xor(qs, 32, 64);
+  const float qbias = kBias * qs;  // per head col: 136 * sum of the query operand
+  float m_i = -INFINITY, l_part = 0.f;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = as_bf16x8(uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const size_t head_bytes = (size_t)kPageSize * D / 2;
+  for (int blk = t0; blk < t1; blk += 32) {
+    const int page = block_table[(size_t)b * mpps + blk / kPageSize];
+    const int off = blk % kPageSize;  // 0 or 32
+    const size_t hb_off = ((size_t)page * nkv + h) * head_bytes;
+    const size_t sc_off = ((size_t)page * nkv + h) * kPageSize + off;
+    // key tiles (two 16-token tiles) and value tiles (D/64 channel groups)
+    uint32_t kw[2][D / 32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint8_t* p = kv.k_codes + hb_off + (size_t)((off >> 4) + u) * (8 * D) + (size_t)lane * (D / 8);
+      if constexpr (D == 128) {
+        const uint4 v = *(const uint4*)p;
+        kw[u][0] = v.x; kw[u][1] = v.y; kw[u][2] = v.z; kw[u][3] = v.w;
+      } else {
+        const uint2 v = *(const uint2*)p;
+        kw[u][0] = v.x; kw[u][1] = v.y;
+      }
+    }
+    uint4 vw[D / 64];
+#pragma unroll
+    for (int cg = 0; cg < D / 64; ++cg)
+      vw[cg] = *(const uint4*)(kv.v_codes + hb_off + (size_t)((off >> 5) * (D / 64) + cg) * 1024 + (size_t)lane * 16);
+    float ks[2][4], vs[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint2 k2 = *(const uint2*)(kv.k_scales + sc_off + 16 * u + 4 * grp);
+      const uint2 v2 = *(const uint2*)(kv.v_scales + sc_off + 16 * u + 4 * grp);
+      ks[u][0] = half_bits_to_f32(k2.x & 0xFFFF); ks[u][1] = half_bits_to_f32(k2.x >> 16);
+      ks[u][2] = half_bits_to_f32(k2.y & 0xFFFF); ks[u][3] = half_bits_to_f32(k2.y >> 16);
+      vs[u][0] = half_bits_to_f32(v2.x & 0xFFFF); vs[u][1] = half_bits_to_f32(v2.x >> 16);
+      vs[u][2] = half_bits_to_f32(v2.y & 0xFFFF); vs[u][3] = half_bits_to_f32(v2.y >> 16);
+    }
+    // scores
+    float z[2][4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const bf16x8 kb = widen_word(kw[u][s]);
+        d = mfma16(kb, qh[s], d);
+        if constexpr (QF32) d = mfma16(kb, ql[s], d);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = blk + 16 * u + 4 * grp + r;
+        z[u][r] = t < t1 ? (d[r] - qbias) * ks[u][r] * scale : -INFINITY;
+        mloc = fmaxf(mloc, z[u][r]);
+      }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_i, mloc);
+    const float alpha = expf(m_i - m_new);
+    float psum = 0.f;
+    uint16_t ph[8], pl[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = expf(z[u][r] - m_new);
+        psum += p;
+        // tokens past the end may hold stale scales: keep them out of p.v
+        const float pv = z[u][r] == -INFINITY ? 0.f : p * vs[u][r];
+        split_bf16(pv, &ph[4 * u + r], &pl[4 * u + r]);
+      }
+    }
+    l_part = l_part * alpha + psum;
+    m_i = m_new;
+    const bf16x8 pah = as_bf16x8(uint4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])});
+    const bf16x8 pal = as_bf16x8(uint4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])});
+    // rescale the p.v accumulators: row 4 (L/16) + r belongs to head 4 grp + r
+    float al[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[c][r] *= al[r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc1[r] *= al[r];
+#pragma unroll
+    for (int cg = 0; cg < D / 64; ++cg)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const bf16x8 vb = widen_word(word_of(vw[cg], c4));
+        acc[cg * 4 + c4] = mfma16(pah, vb, acc[cg * 4 + c4]);
+        acc[cg * 4 + c4] = mfma16(pal, vb, acc[cg * 4 + c4]);
+      }
+    acc1 = mfma16(pah, ones, acc1);
+    acc1 = mfma16(pal, ones, acc1);
+  }
+  // finalize this chunk's partials
+  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  float* out = apart + (((size_t)b * nq + h * G) * nsplit + sp) * (D + 2);
+  const size_t head_stride = (size_t)nsplit * (D + 2);
+  if (grp == 0 && col < G) {
+    out[col * head_stride + 0] = m_i;
+    out[col * head_stride + 1] = l_tot;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * grp + r;
+    if (i < G) {
+#pragma unroll
+      for (int cg = 0; cg < D / 64; ++cg)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int c = cg * 64 + c4 * 16 + col;
+          out[i * head_stride + 2 + c] = acc[cg * 4 + c4][r] - kBias * acc1[r];
+        }
+    }
+  }
+}
+
+// Merge of the split partials + inverse block Hadamard.  One block of D
+// threads per (query head, sequence).  Writes fp32 output, or bf16 output
+// plus the group sums of the O projection input.
+template <int D>
+__global__ __launch_bounds__(128) void attn_merge_kernel(
+    const float* __restrict__ apart, const int32_t* __restrict__ lens, int len_add, int nq,
+    int chunk, int nsplit, int hb, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
+    float* __restrict__ gsum, int G) {
+  const int i = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int L = lens[b] + len_add;
+  const int nsp = (L + chunk - 1) / chunk;
+  const float* base = apart + ((size_t)b * nq + i) * nsplit * (D + 2);
+  float m = -INFINITY;
+  for (int sp = 0; sp < nsp; ++sp) m = fmaxf(m, base[sp * (D + 2)]);
+  float l = 0.f, a = 0.f;
+  for (int sp = 0; sp < nsp; ++sp) {
+    const float w = expf(base[sp * (D + 2)] - m);
+    l += w * base[sp * (D + 2) + 1];
+    a += w * base[sp * (D + 2) + 2 + c];
+  }
+  float o[1] = {l > 0.f ? a / l : 0.f};
+  // inverse rotation (the normalized Sylvester matrix is its own inverse)
+  const int lane = c & 63;
+  for (int hop = 1; hop < hb; hop <<= 1) {
+    const float p = __shfl_xor(o[0], hop, 64);
+    o[0] = (lane & hop) ? p - o[0] : o[0] + p;
+  }
+  o[0] *= 1.0f / sqrtf((float)hb);
+  if (out_f32) out_f32[((size_t)b * nq + i) * D + c] = o[0];
+  if (out_bf16) {
+    const uint16_t ob = f32_to_bf16_bits(o[0]);
+    out_bf16[(size_t)b * nq * D + (size_t)i * D + c] = ob;
+    // group sums: groups of G (64 or 128) channels inside the head
+    float s = wave_sum(bf16_bits_to_f32(ob));
+    __shared__ float red[2];
+    if (lane == 0) red[c >> 6] = s;
+    __syncthreads();
+    if (c == 0) {
+      const int gpr = D / G;  // groups per head
+      for (int g2 = 0; g2 < gpr; ++g2) {
+        float t = 0.f;
+        for (int w = g2 * (G / 64); w < (g2 + 1) * (G / 64); ++w) t += red[w];
+        gsum[(size_t)(i * gpr + g2) * kMaxBatch + b] = t;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+#define FUTX_LAUNCH_CHECK()                                   \
+  do {                                                        \
+    hipError_t e_ = hipGetLastError();                        \
+    if (e_ != hipSuccess) return e_;                          \
+  } while (0)
+
+hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* act, float* invr,
+                           hipStream_t st) {
+  prep_act_kernel<<<B, 256, 0, st>>>(x, H, eps, act, invr);
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float* gsum, hipStream_t st) {
+  gsum_kernel<<<dim3(K / G, B), 64, 0, st>>>(act, K, G, gsum);
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+GemmPlan gemm_plan(int N, int K) {
+  GemmPlan p;
+  const int kblocks = K / 128, ntiles = N / 16;
+  int s = (2048 + ntiles - 1) / ntiles;
+  s = s < 1 ? 1 : s;
+  s = s > 16 ? 16 : s;
+  s = s > kblocks ? kblocks : s;
+  p.kbps = (kblocks + s - 1) / s;
+  p.splits = (kblocks + p.kbps - 1) / p.kbps;
+  return p;
+}
+
+hipError_t launch_gemm_partial(const void* wpk, const void* wsc, const uint16_t* act,
+                               const float* gsum, int B, int N, int K, int G, float* part,
+                               const GemmPlan& plan, hipStream_t st) {
+  const int waves = (N / 16) * plan.splits;
+  const dim3 grid((waves + 3) / 4), block(256);
+  const uint4* w = (const uint4*)wpk;
+  const uint16_t* s = (const uint16_t*)wsc;
+  if (G == 128) {
+    if (B <= 16)
+      gemm_partial_kernel<128, 1><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
+    else
+      gemm_partial_kernel<128, 2><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
+  } else {
+    if (B <= 16)
+      gemm_partial_kernel<64, 1><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
+    else
+      gemm_partial_kernel<64, 2><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
+  }
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_reduce(const float* part, int S, int B, int N, const float* rowscale,
+                         const float* resid, float* out, int gateup_inter, hipStream_t st) {
+  const int total = B * N;
+  reduce_kernel<<<(total + 255) / 256, 256, 0, st>>>(part, S, B, N, rowscale, resid, out, gateup_inter);
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_swiglu(const float* part, int S, int B, int I, int G, const float* invr,
+                         uint16_t* act, float* gsum, hipStream_t st) {
+  swiglu_kernel<<<dim3(I / G, B), G, 0, st>>>(part, S, B, I, G, invr, act, gsum);
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_kv_append(const float* k, const float* v, const int32_t* positions,
+                            const int32_t* slots, int n, uint32_t flags, int D, int hb,
+                            float theta, const KVPtrs& kv, hipStream_t st) {
+  const dim3 grid(n, kv.nkv);
+  if (D == 128)
+    kv_append_kernel<128><<<grid, 64, 0, st>>>(k, v, positions, slots, flags, hb, theta, kv);
+  else
+    kv_append_kernel<64><<<grid, 64, 0, st>>>(k, v, positions, slots, flags, hb, theta, kv);
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_post_qkv(const float* qkv, int B, int nq, int D, const int32_t* cached_lens,
+                           const int32_t* block_table, int mpps, int hb, float theta, float* qrot,
+                           const KVPtrs& kv, hipStream_t st) {
+  const dim3 grid(nq + kv.nkv, B);
+  if (D == 128)
+    post_qkv_kernel<128><<<grid, 64, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, hb, theta, qrot, kv);
+  else
+    post_qkv_kernel<64><<<grid, 64, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, hb, theta, qrot, kv);
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+AttnPlan attn_plan(int B, int nkv, int max_context) {
+  AttnPlan p;
+  const int pages = (max_context + kPageSize - 1) / kPageSize;
+  const long work = (long)B * nkv * pages;  // page-sized work items
+  int cp = (int)((work + 2047) / 2048);
+  cp = cp < 1 ? 1 : cp;
+  p.chunk = cp * kPageSize;
+  p.nsplit = (max_context + p.chunk - 1) / p.chunk;
+  if (p.nsplit < 1) p.nsplit = 1;
+  return p;
+}
+
+hipError_t launch_attention(const void* q, bool q_f32, const int32_t* lens, int len_add,
+                            const int32_t* block_table, int mpps, int B, int nq, int D,
+                            const AttnPlan& plan, const KVPtrsConst& kv, float* apart,
+                            hipStream_t st) {
+  const dim3 grid(plan.nsplit, kv.nkv, B);
+  const float scale = 1.0f / sqrtf((float)D);
+#define FUTX_ATTN(DD, QF)                                                                          \
+  attn_split_kernel<DD, QF><<<grid, 64, 0, st>>>(q, lens, len_add, block_table, mpps, nq, plan.chunk, \
+                                                 plan.nsplit, scale, kv, apart)
+  if (D == 128) {
+    if (q_f32) FUTX_ATTN(128, true); else FUTX_ATTN(128, false);
+  } else {
+    if (q_f32) FUTX_ATTN(64, true); else FUTX_ATTN(64, false);
+  }
+#undef FUTX_ATTN
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+hipError_t launch_attn_merge(const float* apart, const int32_t* lens, int len_add, int B, int nq,
+                             int D, const AttnPlan& plan, int hb, float* out_f32,
+                             uint16_t* out_bf16, float* gsum, int G, hipStream_t st) {
+  const dim3 grid(nq, B);
+  if (D == 128)
+    attn_merge_kernel<128><<<grid, 128, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, gsum, G);
+  else
+    attn_merge_kernel<64><<<grid, 64, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, gsum, G);
+  FUTX_LAUNCH_CHECK();
+  return hipSuccess;
+}
+
+}  // namespace futx

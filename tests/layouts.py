@@ -1,0 +1,82 @@
+"""Test-side decoders of the device layouts (written from the layout
+description, independent of the library and of the oracle).
+
+Weights: packed[nt][kb][L][16 bytes]; word s (bytes 4s..4s+3, little endian)
+of lane L holds row nt*16 + L%16, inputs kb*128 + 32 s + 8 (L // 16) + e;
+element e = 2j sits in bits 4j..4j+3, e = 2j+1 in bits 16+4j..16+4j+3, each
+as code + 8.  GATEUP physical tile 2t = gate rows 16t.., 2t+1 = up rows 16t..
+
+KV cache per (page, KV head): keys [tt][L][D/8 bytes] with token tt*16 + L%16
+and word s = channels 32 s + 8 (L//16) + e; values [tb][cg][L][16 bytes] with
+word c4 = channel cg*64 + 16 c4 + L%16 and element e = token tb*32 + tok(L//16, e),
+tok(g, e) = 4g + e (e < 4) else 16 + 4g + e - 4.
+"""
+
+import numpy as np
+
+
+def _nibbles(words):
+    """uint32 [...] -> codes int8 [..., 8] in element order e = 0..7."""
+    out = np.empty(words.shape + (8,), np.int8)
+    for e in range(8):
+        bit = 16 + 4 * (e // 2) if e % 2 else 4 * (e // 2)
+        out[..., e] = ((words >> np.uint32(bit)) & np.uint32(15)).astype(np.int16) - 8
+    return out
+
+
+def decode_weights(packed, n, k):
+    """Device-order bytes of an [n][k] projection -> codes int8 [n_phys][k]."""
+    b = np.asarray(packed, np.uint8).reshape(n // 16, k // 128, 4, 16, 4, 4)  # nt kb g i s byte
+    words = b.copy().view(np.uint32)[..., 0]  # nt kb g i s
+    codes = _nibbles(words)  # nt kb g i s e
+    codes = codes.transpose(0, 3, 1, 4, 2, 5)  # nt i kb s g e
+    return codes.reshape(n, k)
+
+
+def gateup_logical_order(phys, inter):
+    """Rows of a GATEUP matrix in physical order -> logical order (gate rows then up rows)."""
+    p = np.asarray(phys)
+    n = p.shape[0]
+    rows = np.arange(n)
+    tile, i = rows // 16, rows % 16
+    logical = (tile % 2) * inter + (tile // 2) * 16 + i
+    out = np.empty_like(p)
+    out[logical] = p
+    return out
+
+
+def decode_k_page(kbytes, d):
+    """Key codes of one (page, head): bytes [64 * d / 2] -> codes int8 [64][d]."""
+    b = np.asarray(kbytes, np.uint8).reshape(4, 4, 16, d // 32, 4)  # tt g i s byte
+    words = b.copy().view(np.uint32)[..., 0]  # tt g i s
+    codes = _nibbles(words)  # tt g i s e
+    codes = codes.transpose(0, 2, 3, 1, 4)  # tt i s g e
+    return codes.reshape(64, d)
+
+
+def decode_v_page(vbytes, d):
+    """Value codes of one (page, head): bytes [64 * d / 2] -> codes int8 [64][d]."""
+    b = np.asarray(vbytes, np.uint8).reshape(2, d // 64, 4, 16, 4, 4)  # tb cg g i c4 byte
+    words = b.copy().view(np.uint32)[..., 0]  # tb cg g i c4
+    codes = _nibbles(words)  # tb cg g i c4 e
+    out = np.empty((64, d), np.int8)
+    for tb in range(2):
+        for g in range(4):
+            for e in range(8):
+                t = tb * 32 + (4 * g + e if e < 4 else 16 + 4 * g + e - 4)
+                for cg in range(d // 64):
+                    for c4 in range(4):
+                        ch = cg * 64 + 16 * c4 + np.arange(16)
+                        out[t, ch] = codes[tb, cg, g, :, c4, e]
+    return out
+
+
+def decode_cache(k_codes, v_codes, k_scales, v_scales, num_pages, nkv, d):
+    """Whole cache -> (k codes [pages][nkv][64][d], k scales fp16 [pages][nkv][64], v codes, v scales)."""
+    kc = np.asarray(k_codes, np.uint8).reshape(num_pages, nkv, 64 * d // 2)
+    vc = np.asarray(v_codes, np.uint8).reshape(num_pages, nkv, 64 * d // 2)
+    K = np.stack([np.stack([decode_k_page(kc[p, h], d) for h in range(nkv)]) for p in range(num_pages)])
+    V = np.stack([np.stack([decode_v_page(vc[p, h], d) for h in range(nkv)]) for p in range(num_pages)])
+    ks = np.asarray(k_scales).view(np.float16).reshape(num_pages, nkv, 64)
+    vs = np.asarray(v_scales).view(np.float16).reshape(num_pages, nkv, 64)
+    return K, ks, V, vs

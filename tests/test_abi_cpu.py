@@ -1,0 +1,154 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+of include/futx.h, validates arguments before touching the GPU, and its host
+packer writes exactly the codes and scales of the oracle's quantizer in the
+documented device order (decoded by tests/layouts.py)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from int4_weight_kv_amd import workload as W
+from tests import layouts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "futx.h")
+
+
+@pytest.fixture(scope="module")
+def fx():
+    from int4_weight_kv_amd import futx
+
+    return futx
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(futx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(fx):
+    names = _declared()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(fx.LIBRARY_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    nm = subprocess.run(["nm", "-D", "--defined-only", fx.LIBRARY_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (futx_\w+)", nm))
+    assert set(names) <= exported
+    assert set(fx.EXPORTED) == set(names)
+
+
+def test_argument_validation(fx):
+    d = fx.make_dims(W.TINY)
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_packed_sizes(W.Dims(256, 4, 2, 96, 768, 64, 32), "qkv")
+    assert e.value.status == fx.FUTX_E_UNSUPPORTED
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_packed_sizes(W.Dims(256, 4, 2, 64, 768, 64, 48), "qkv")
+    assert e.value.status == fx.FUTX_E_UNSUPPORTED
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_packed_sizes(W.Dims(0, 4, 2, 64, 768, 64, 32), "qkv")
+    assert e.value.status == fx.FUTX_E_ARG
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_packed_sizes(W.TINY, 7)
+    assert e.value.status == fx.FUTX_E_ARG
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_decode_workspace_size(W.TINY, 33, 100)
+    assert e.value.status == fx.FUTX_E_ARG
+    # decode_block rejects a null cache before anything reaches the GPU
+    cache = fx.futx_kv_cache(None, None, None, None, 0)
+    wts = fx.make_block_weights((None, None), (None, None), (None, None), (None, None))
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_decode_block(W.TINY, wts, 1, None, None, None, 1, 1, cache, None, 0, stream=0)
+    assert e.value.status == fx.FUTX_E_ARG
+    assert "cache" in fx.futx_last_error()
+
+
+def test_sizes(fx):
+    pb, sb = fx.futx_packed_sizes(W.LLAMA8B, "gateup")
+    assert pb == 2 * 14336 * 4096 // 2 and sb == 2 * 14336 * 32 * 2
+    cb, sb = fx.futx_kv_cache_sizes(W.LLAMA8B, 10)
+    assert cb == 10 * 8 * 64 * 64 and sb == 10 * 8 * 64 * 2
+    assert fx.futx_decode_workspace_size(W.LLAMA8B, 32, 8192) > fx.futx_decode_workspace_size(W.LLAMA8B, 1, 2048)
+
+
+def _host_pack(fx, dims, proj, w, gain):
+    pb, sb = fx.futx_packed_sizes(dims, proj)
+    packed = np.zeros(pb, np.uint8)
+    scales = np.zeros(sb // 2, np.uint16)
+    fx.futx_pack_weights_host(dims, proj, w, gain, packed, scales)
+    return packed, scales
+
+
+@pytest.mark.parametrize("proj", ["qkv", "o", "gateup", "down"])
+def test_host_pack_bit_exact_tiny(fx, proj):
+    wl = W.tiny()
+    w = W.block_weights(wl, 0)
+    d = wl.dims
+    mats = {"qkv": (w["wqkv"], w["gain_attn"]), "o": (w["wo"], None),
+            "gateup": (np.concatenate([w["wgate"], w["wup"]]), w["gain_ffn"]), "down": (w["wdown"], None)}
+    m, g = mats[proj]
+    packed, scales = _host_pack(fx, d, proj, m, g)
+    n, k = m.shape
+    codes = layouts.decode_weights(packed, n, k)
+    sc = scales.view(np.float16).reshape(n, k // d.w_group)
+    if proj == "gateup":
+        codes = layouts.gateup_logical_order(codes, d.intermediate)
+        sc = layouts.gateup_logical_order(sc, d.intermediate)
+    folded = m if g is None else oracle.fold_gain(m, g)
+    want_q, want_s = oracle.quantize_weight_rtn(folded, d.w_group)
+    np.testing.assert_array_equal(codes, want_q)
+    np.testing.assert_array_equal(sc.view(np.uint16), want_s.view(np.uint16))
+
+
+def test_host_pack_edge_values(fx):
+    """Ties, zero groups, fp16-subnormal scales, the -8 code from external
+    codes cannot arise; large but representable scales."""
+    d = W.TINY
+    r = np.random.default_rng(11)
+    w = (r.standard_normal((256, 256)) * 0.02).astype(np.float32)
+    w[0, :64] = 0.0
+    w[1, :64] = np.float32(1e-6) * r.standard_normal(64).astype(np.float32)  # subnormal fp16 scale
+    w[2, :64] = np.float32(1e-9)  # rounds to a zero scale
+    w[3, :8] = [7, 3.5, -2.5, 0.5, 0, 0, 0, 0]
+    w[4, :64] = np.float32(4.0e5)  # scale 57142.86 (fp16-representable range)
+    w[5, :64] = np.linspace(-1, 1, 64, dtype=np.float32)
+    packed, scales = _host_pack(fx, d, "o", w, None)
+    codes = layouts.decode_weights(packed, 256, 256)
+    want_q, want_s = oracle.quantize_weight_rtn(w, 64)
+    np.testing.assert_array_equal(codes, want_q)
+    np.testing.assert_array_equal(scales.view(np.float16).reshape(256, 4).view(np.uint16), want_s.view(np.uint16))
+    w[6, 0] = np.float32(1e6)  # max|w|/7 overflows fp16
+    with pytest.raises(fx.FutxError) as e:
+        _host_pack(fx, d, "o", w, None)
+    assert e.value.status == fx.FUTX_E_RANGE
+
+
+def test_host_pack_bit_exact_8b_slice(fx):
+    """A full-width 8B-shape O projection (K = 4096, group 128)."""
+    wl = W.llama8b()
+    r = np.random.default_rng(12)
+    w = (r.standard_normal((4096, 4096)) * 0.02).astype(np.float32)
+    packed, scales = _host_pack(fx, wl.dims, "o", w, None)
+    codes = layouts.decode_weights(packed, 4096, 4096)
+    want_q, want_s = oracle.quantize_weight_rtn(w, 128)
+    np.testing.assert_array_equal(codes, want_q)
+    np.testing.assert_array_equal(scales.view(np.float16).reshape(4096, 32).view(np.uint16), want_s.view(np.uint16))
+
+
+def test_fold_head_matches_oracle(fx):
+    r = np.random.default_rng(13)
+    vocab, hidden = 300, 256
+    w = W.to_bf16_values((r.standard_normal((vocab, hidden)) * 0.02).astype(np.float32))
+    gain = r.uniform(0.5, 1.5, hidden).astype(np.float32)
+    wbits = (w.view(np.uint32) >> 16).astype(np.uint16)
+    out = np.zeros((vocab, hidden), np.uint16)
+    fx.futx_fold_head(vocab, hidden, wbits, gain, out)
+    got = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(got, oracle.fold_head(w, gain))

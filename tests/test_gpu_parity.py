@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+* packing and the KV quantizer (identical fp32 inputs): bit-exact;
+* the full cache write (RoPE + rotation in fp32 on the GPU, fp64 in the
+  oracle): equal except codes one step apart where the oracle's value sits
+  within 1e-3 of a rounding midpoint, and scales one fp16 step apart near an
+  fp16 midpoint; such exceptions below 1e-4 of the elements;
+* INT4 projections: fp32-accumulation level agreement;
+* block outputs: max|gpu - oracle| <= 2e-3 max|oracle| + 1e-3.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from int4_weight_kv_amd import workload as W
+from tests import layouts
+from tests.gpu_common import BlockCase, block_tolerance, say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from int4_weight_kv_amd import futx
+
+    return futx
+
+
+@pytest.fixture(scope="module")
+def DB(F):
+    from int4_weight_kv_amd import block
+
+    return block
+
+
+# ---------------------------------------------------------------- packing
+
+
+@pytest.mark.parametrize("shape,proj", [("tiny", "qkv"), ("tiny", "gateup"), ("tiny", "down"), ("8b", "o"),
+                                        ("8b", "gateup")])
+def test_pack_device_bit_exact(F, DB, shape, proj):
+    wl = W.tiny() if shape == "tiny" else W.llama8b()
+    d = wl.dims
+    w = W.block_weights(wl, 0)
+    mats = {"qkv": (w["wqkv"], w["gain_attn"]), "o": (w["wo"], None),
+            "gateup": (np.concatenate([w["wgate"], w["wup"]]), w["gain_ffn"]), "down": (w["wdown"], None)}
+    m, g = mats[proj]
+    say("pack", shape, proj, m.shape)
+    pp = DB.pack_projection(d, proj, m, g)
+    n, k = m.shape
+    canon = np.zeros((n, k // 2), np.uint8)
+    csc = np.zeros((n, k // d.w_group), np.uint16)
+    F.futx_unpack_weights(d, proj, pp.packed, pp.scales, canon, csc)
+    folded = m if g is None else oracle.fold_gain(m, g)
+    q, s = oracle.quantize_weight_rtn(folded, d.w_group)
+    np.testing.assert_array_equal(canon, oracle.pack_nibbles(q))
+    np.testing.assert_array_equal(csc, s.view(np.uint16))
+    # raw device bytes through the independent layout decoder
+    raw = layouts.decode_weights(pp.packed.cpu().numpy(), n, k)
+    if proj == "gateup":
+        raw = layouts.gateup_logical_order(raw, d.intermediate)
+    np.testing.assert_array_equal(raw, q)
+
+
+# ---------------------------------------------------------------- KV append
+
+
+def _cache_tokens(cache_host, dims, num_pages, slots):
+    kc, vc, ks, vs = cache_host
+    K, KS, V, VS = layouts.decode_cache(kc, vc, ks, vs, num_pages, dims.n_kv_heads, dims.head_dim)
+    p, o = slots // 64, slots % 64
+    return K[p, :, o], KS[p, :, o], V[p, :, o], VS[p, :, o]
+
+
+@pytest.mark.parametrize("shape", ["tiny", "8b"])
+def test_kv_append_quantizer_bit_exact(F, DB, shape):
+    """flags = 0: the stored codes and scales equal the oracle's quantizer on
+    the same fp32 inputs, bit for bit, including ties and zero rows."""
+    wl = W.tiny() if shape == "tiny" else W.llama8b()
+    d = wl.dims
+    r = np.random.default_rng(21)
+    n, num_pages = 300, 9
+    k = r.standard_normal((n, d.n_kv_heads, d.head_dim)).astype(np.float32)
+    v = (r.standard_normal((n, d.n_kv_heads, d.head_dim)) * 3).astype(np.float32)
+    k[0, 0] = 0.0  # zero row -> scale 0, codes 0
+    k[1, 0, :8] = [7, 3.5, -2.5, 0.5, 0, 0, 0, 0]  # exact ties
+    k[1, 0, 8:] = 0.0
+    v[2, :] = np.float32(1e-9)  # rounds to a zero scale
+    slots = r.permutation(num_pages * 64)[:n].astype(np.int32)
+    cache = DB.DeviceKVCache(d, num_pages)
+    say("kv_append flags=0", shape)
+    cache.append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), None,
+                 torch.from_numpy(slots).cuda(), flags=0)
+    torch.cuda.synchronize()
+    K, KS, V, VS = _cache_tokens(cache.host_copy(), d, num_pages, slots)
+    qk, sk = oracle.quantize_kv_token(k)
+    qv, sv = oracle.quantize_kv_token(v)
+    np.testing.assert_array_equal(K, qk)
+    np.testing.assert_array_equal(V, qv)
+    np.testing.assert_array_equal(KS.view(np.uint16), sk.view(np.uint16))
+    np.testing.assert_array_equal(VS.view(np.uint16), sv.view(np.uint16))
+
+
+def _flip_tolerant(got_q, got_s, x64, tag):
+    """Compare GPU codes/scales with the oracle's fp32 recipe applied to the
+    oracle's fp64 values.  Allowed differences (fp32 on the GPU vs fp64 in
+    the oracle before the fp32 quantizer):
+      * a scale one fp16 step away, only where the oracle's fp32(max/7) lies
+        within 2**-20 (relative) of the midpoint of the two fp16 values;
+      * a code one step away, only where the oracle's value / scale lies
+        within 1e-3 of a half-integer (1e-2 on rows whose scale moved), and on
+        at most 1e-4 of the elements."""
+    x32 = x64.astype(np.float32)
+    want_q, want_s = oracle.quantize_kv_token(x32)
+    s_bad = got_s.view(np.uint16) != want_s.view(np.uint16)
+    if np.any(s_bad):
+        step = np.abs(got_s.view(np.uint16)[s_bad].astype(np.int64) - want_s.view(np.uint16)[s_bad].astype(np.int64))
+        assert np.all(step == 1), tag
+        s32 = (np.max(np.abs(x32), axis=-1) / np.float32(7)).astype(np.float32)[s_bad].astype(np.float64)
+        mid = (got_s[s_bad].astype(np.float64) + want_s[s_bad].astype(np.float64)) / 2
+        assert np.all(np.abs(s32 - mid) <= 2.0 ** -20 * s32), (tag, s32, mid)
+    q_bad = got_q != want_q
+    if np.any(q_bad):
+        assert np.all(np.abs(got_q.astype(np.int16) - want_q)[q_bad] <= 1), tag
+        sf = want_s.astype(np.float64)[..., None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = x64 / sf
+        frac = np.abs(r - np.floor(r) - 0.5)
+        lim = np.where(np.broadcast_to(s_bad[..., None], q_bad.shape), 1e-2, 1e-3)
+        assert np.all(frac[q_bad] < lim[q_bad]), tag
+    assert q_bad.mean() <= 1e-4, (tag, q_bad.mean())
+    return int(q_bad.sum()), int(s_bad.sum())
+
+
+@pytest.mark.parametrize("shape", ["tiny", "8b", "8b-outliers"])
+def test_kv_append_full_chain(F, DB, shape):
+    """RoPE + block Hadamard + quantization at arbitrary positions."""
+    wl = {"tiny": W.tiny(), "8b": W.llama8b(), "8b-outliers": W.llama8b_ragged(1)}[shape]
+    d = wl.dims
+    n = 700
+    k, v = W.history(wl, 0, 0, n)
+    r = np.random.default_rng(22)
+    pos = r.integers(0, 9000, n).astype(np.int32)
+    num_pages = 16
+    slots = r.permutation(num_pages * 64)[:n].astype(np.int32)
+    cache = DB.DeviceKVCache(d, num_pages)
+    say("kv_append rope+hadamard", shape)
+    cache.append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(pos).cuda(),
+                 torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    K, KS, V, VS = _cache_tokens(cache.host_copy(), d, num_pages, slots)
+    kr, vr = oracle.rotate_kv(k.astype(np.float64), v.astype(np.float64), pos[:, None], d)
+    fk = _flip_tolerant(K, KS, kr, "keys")
+    fv = _flip_tolerant(V, VS, vr, "values")
+    say("boundary flips (codes, scales): keys", fk, "values", fv)
+
+
+# ---------------------------------------------------------------- projections
+
+
+@pytest.mark.parametrize("shape", ["tiny", "8b"])
+@pytest.mark.parametrize("batch", [1, 5, 16, 17, 32])
+def test_int4_linear(F, DB, shape, batch):
+    wl = W.tiny() if shape == "tiny" else W.llama8b()
+    d = wl.dims
+    w = W.block_weights(wl, 0)
+    r = np.random.default_rng(23 + batch)
+    for proj, m, g in (("qkv", w["wqkv"], w["gain_attn"]), ("o", w["wo"], None),
+                       ("gateup", np.concatenate([w["wgate"], w["wup"]]), w["gain_ffn"]), ("down", w["wdown"], None)):
+        if shape == "8b" and proj in ("qkv", "o") and batch not in (1, 32):
+            continue
+        n, kk = m.shape
+        act = W.to_bf16_values(r.standard_normal((batch, kk)).astype(np.float32))
+        abits = (act.view(np.uint32) >> 16).astype(np.uint16)
+        pp = DB.pack_projection(d, proj, m, g)
+        ws_bytes = F.futx_decode_workspace_size(d, batch, 1)
+        ws = DB.device_buffer(ws_bytes)
+        out = torch.empty((batch, n), dtype=torch.float32, device="cuda")
+        say("int4_linear", shape, proj, "batch", batch)
+        F.futx_int4_linear(d, proj, (pp.packed, pp.scales), batch, torch.from_numpy(abits).cuda(), out, ws,
+                           ws_bytes)
+        torch.cuda.synchronize()
+        folded = m if g is None else oracle.fold_gain(m, g)
+        q, s = oracle.quantize_weight_rtn(folded, d.w_group)
+        ref = act.astype(np.float64) @ oracle.dequant_weight(q, s, d.w_group).T
+        err = np.max(np.abs(out.cpu().numpy() - ref))
+        # fp32 accumulation over K inputs: far below the block tolerance
+        assert err <= 1e-5 * np.max(np.abs(ref)) * np.sqrt(kk / 128) + 1e-6, (proj, err)
+
+
+# ---------------------------------------------------------------- attention
+
+
+@pytest.mark.parametrize("shape,lens", [("tiny", [1]), ("tiny", [63, 64, 65, 200]), ("8b", [2048]),
+                                        ("8b", [1, 31, 32, 33, 700, 4097]), ("70b", [129, 1000])])
+def test_decode_attention(F, DB, shape, lens):
+    wl = {"tiny": W.tiny(len(lens)), "8b": W.llama8b(len(lens)), "70b": W.llama70b(len(lens))}[shape]
+    d = wl.dims
+    lens = np.array(lens, np.int32)  # tokens to read
+    layout = W.page_layout(wl, lens, extra_tokens=0, seed=5, spare_pages=2)
+    r = np.random.default_rng(24)
+    cache = DB.DeviceKVCache(d, layout.num_pages)
+    hist = []
+    for b, L in enumerate(lens):
+        kr = r.standard_normal((L, d.n_kv_heads, d.head_dim)).astype(np.float32)
+        vr = (r.standard_normal((L, d.n_kv_heads, d.head_dim)) * 2).astype(np.float32)
+        slots = (layout.block_table[b, np.arange(L) // 64] * 64 + np.arange(L) % 64).astype(np.int32)
+        cache.append(torch.from_numpy(kr).cuda(), torch.from_numpy(vr).cuda(), None, torch.from_numpy(slots).cuda(),
+                     flags=0)
+        hist.append((kr, vr))
+    q = W.to_bf16_values(r.standard_normal((len(lens), d.n_heads, d.head_dim)).astype(np.float32) * 2)
+    qbits = (q.view(np.uint32) >> 16).astype(np.uint16)
+    ws_bytes = F.futx_decode_workspace_size(d, len(lens), int(lens.max()))
+    ws = DB.device_buffer(ws_bytes)
+    out = torch.empty((len(lens), d.n_heads, d.head_dim), dtype=torch.float32, device="cuda")
+    say("decode_attention", shape, lens.tolist())
+    F.futx_decode_attention(d, len(lens), torch.from_numpy(qbits).cuda(), torch.from_numpy(lens).cuda(),
+                            torch.from_numpy(layout.block_table).cuda(), layout.block_table.shape[1],
+                            int(lens.max()), cache.c_cache, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b, (kr, vr) in enumerate(hist):
+        qk, sk = oracle.quantize_kv_token(kr)
+        qv, sv = oracle.quantize_kv_token(vr)
+        kh = qk * sk[..., None].astype(np.float64)
+        vh = qv * sv[..., None].astype(np.float64)
+        ref = oracle.decode_attention(q[b].astype(np.float64), kh, vh, d.had_block)
+        err = np.max(np.abs(got[b] - ref))
+        tol = block_tolerance(ref)
+        say("  b", b, "L", int(lens[b]), "max err %.3g tol %.3g" % (err, tol))
+        assert err <= tol
+
+
+# ---------------------------------------------------------------- whole block
+
+
+def _check_block(case, reps=2):
+    outs = case.run_gpu(reps=reps)
+    y = case.run_oracle()
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])  # deterministic: bitwise repeatable
+    err = float(np.max(np.abs(outs[0] - y)))
+    tol = block_tolerance(y)
+    say(case.wl.name, "block max err %.4g tol %.4g" % (err, tol))
+    assert err <= tol
+    return outs[0], y
+
+
+def test_block_tiny():
+    case = BlockCase(W.tiny())
+    _check_block(case)
+    # the new token is in the cache at position cached_lens (flip-tolerant)
+    d = case.dims
+    L = int(case.lens[0])
+    slot = np.array([case.layout.slot(0, L)], np.int32)
+    K, KS, V, VS = _cache_tokens(case.gpu_cache, d, case.layout.num_pages, slot)
+    oc = case.oracle_caches[0]
+    assert np.mean(K[0] != oc.k_codes[L]) <= 0.02 and np.mean(V[0] != oc.v_codes[L]) <= 0.02
+
+
+@pytest.mark.parametrize("batch,lens", [(3, "fixed:0"), (4, "uniform:1:200")])
+def test_block_tiny_ragged(batch, lens):
+    wl = W.Workload(f"tiny-ragged-b{batch}-{lens}", W.TINY, batch, lens)
+    _check_block(BlockCase(wl))
+
+
+def test_block_8b():
+    _check_block(BlockCase(W.llama8b()), reps=1)
+
+
+@pytest.mark.parametrize("batch", [1, 4, 8, 16, 32])
+def test_block_8b_ragged_outliers(batch):
+    _check_block(BlockCase(W.llama8b_ragged(batch)), reps=1)
