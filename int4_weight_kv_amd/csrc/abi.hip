@@ -71,8 +71,8 @@ futx_status check_proj(futx_proj p) {
 // ---------------------------------------------------------------- workspace
 
 struct Ws {
-  uint16_t* act;   // [32][Kmax] bf16
-  float* gsum;     // [Kmax / G][32]
+  uint16_t* act;   // 3 x [32][Kmax] bf16 (GEMM operand; three terms for the O projection)
+  float2* gsum;    // [Kmax / G][32] exact group sums as (hi, lo)
   float* invr;     // [32]
   float* invr2;    // [32]
   float* part;     // split-K partials
@@ -113,8 +113,8 @@ static Ws carve(const futx_dims& d, int B, int max_ctx, char* base) {
   const int D = d.head_dim, nq = d.n_heads;
   const int nqkv = (d.n_heads + 2 * d.n_kv_heads) * D;
   const int nsplit = (max_ctx + kPageSize - 1) / kPageSize;  // chunk >= one page
-  w.act = (uint16_t*)take((size_t)kMaxBatch * K * 2);
-  w.gsum = (float*)take((size_t)(K / d.w_group) * kMaxBatch * 4);
+  w.act = (uint16_t*)take((size_t)3 * kMaxBatch * K * 2);
+  w.gsum = (float2*)take((size_t)(K / d.w_group) * kMaxBatch * 8);
   w.invr = (float*)take(kMaxBatch * 4);
   w.invr2 = (float*)take(kMaxBatch * 4);
   w.part = (float*)take(part_floats(d, B) * 4);
@@ -288,7 +288,8 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
   STEP(launch_gsum(ws.act, B, H, G, ws.gsum, s));
   // QKV
   GemmPlan gq = gemm_plan(nqkv, H);
-  STEP(launch_gemm_partial(w->qkv.packed, w->qkv.scales, ws.act, ws.gsum, B, nqkv, H, G, ws.part, gq, s));
+  const size_t term = (size_t)kMaxBatch * kmax(d);
+  STEP(launch_gemm_partial(w->qkv.packed, w->qkv.scales, ws.act, 1, term, ws.gsum, B, nqkv, H, G, ws.part, gq, s));
   STEP(launch_reduce(ws.part, gq.splits, B, nqkv, ws.invr, nullptr, ws.qkv, 0, s));
   // RoPE, rotation, INT4 append of the new token; rotated bf16 queries
   STEP(launch_post_qkv(ws.qkv, B, nq, D, cached_lens, block_table, max_pages_per_seq, d.had_block,
@@ -298,20 +299,20 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
   STEP(launch_attention(ws.qrot, true, cached_lens, 1, block_table, max_pages_per_seq, B, nq, D,
                         ap, kvc, ws.apart, s));
   STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act,
-                         ws.gsum, G, s));
+                         term, ws.gsum, G, s));
   // O projection + residual
   GemmPlan go = gemm_plan(H, nq * D);
-  STEP(launch_gemm_partial(w->o.packed, w->o.scales, ws.act, ws.gsum, B, H, nq * D, G, ws.part, go, s));
+  STEP(launch_gemm_partial(w->o.packed, w->o.scales, ws.act, 3, term, ws.gsum, B, H, nq * D, G, ws.part, go, s));
   STEP(launch_reduce(ws.part, go.splits, B, H, nullptr, x, ws.h, 0, s));
   // RMSNorm-2 operand, gate/up + SwiGLU
   STEP(launch_prep_act(ws.h, B, H, d.rms_eps, ws.act, ws.invr2, s));
   STEP(launch_gsum(ws.act, B, H, G, ws.gsum, s));
   GemmPlan gg = gemm_plan(2 * I, H);
-  STEP(launch_gemm_partial(w->gateup.packed, w->gateup.scales, ws.act, ws.gsum, B, 2 * I, H, G, ws.part, gg, s));
+  STEP(launch_gemm_partial(w->gateup.packed, w->gateup.scales, ws.act, 1, term, ws.gsum, B, 2 * I, H, G, ws.part, gg, s));
   STEP(launch_swiglu(ws.part, gg.splits, B, I, G, ws.invr2, ws.act, ws.gsum, s));
   // down projection + residual
   GemmPlan gd = gemm_plan(H, I);
-  STEP(launch_gemm_partial(w->down.packed, w->down.scales, ws.act, ws.gsum, B, H, I, G, ws.part, gd, s));
+  STEP(launch_gemm_partial(w->down.packed, w->down.scales, ws.act, 1, term, ws.gsum, B, H, I, G, ws.part, gd, s));
   STEP(launch_reduce(ws.part, gd.splits, B, H, nullptr, ws.h, x, 0, s));
 #undef STEP
   return FUTX_OK;
@@ -333,7 +334,7 @@ futx_status futx_int4_linear(const futx_dims* dims, futx_proj proj, const futx_q
   hipError_t e;
   GemmPlan g = gemm_plan(ps.n, ps.k);
   if ((e = launch_gsum(act, batch, ps.k, dims->w_group, ws.gsum, s)) != hipSuccess) return hip_fail(e, "gsum");
-  if ((e = launch_gemm_partial(w->packed, w->scales, act, ws.gsum, batch, ps.n, ps.k, dims->w_group,
+  if ((e = launch_gemm_partial(w->packed, w->scales, act, 1, 0, ws.gsum, batch, ps.n, ps.k, dims->w_group,
                                ws.part, g, s)) != hipSuccess)
     return hip_fail(e, "gemm");
   if ((e = launch_reduce(ws.part, g.splits, batch, ps.n, nullptr, nullptr, out,
@@ -366,7 +367,7 @@ futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const ui
                             d.head_dim, ap, kv_cptrs(cache, d.n_kv_heads), ws.apart, s)) != hipSuccess)
     return hip_fail(e, "attention");
   if ((e = launch_attn_merge(ws.apart, lens, 0, batch, d.n_heads, d.head_dim, ap, d.had_block, out,
-                             nullptr, nullptr, d.w_group, s)) != hipSuccess)
+                             nullptr, 0, nullptr, d.w_group, s)) != hipSuccess)
     return hip_fail(e, "merge");
   return FUTX_OK;
 }

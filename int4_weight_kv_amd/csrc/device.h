@@ -10,24 +10,56 @@
 namespace futx {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kMagic = 0x43004300u;  // bf16 pair (128, 128)
-constexpr float kBias = 136.0f;           // 128 + nibble offset 8
+constexpr uint32_t kMagic = 0x41804180u;  // bf16 pair (16, 16): exponent 2^4
+constexpr uint32_t kNibMask = 0x00780078u; // mantissa bits 3..6 of both halves
+constexpr float kBias = 24.0f;             // 16 + nibble offset 8
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One word of 8 nibbles -> 8 bf16 operand elements with values 136 + code.
+__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// One word of 8 nibbles -> 8 bf16 operand elements with values 24 + code
+// (encoding in layout.h).
 __device__ __forceinline__ bf16x8 widen_word(uint32_t w) {
   u32x4 r;
-  r.x = (w & 0x000F000Fu) | kMagic;
-  r.y = ((w >> 4) & 0x000F000Fu) | kMagic;
-  r.z = ((w >> 8) & 0x000F000Fu) | kMagic;
-  r.w = ((w >> 12) & 0x000F000Fu) | kMagic;
+  r.x = (w & kNibMask) | kMagic;
+  r.y = ((w >> 4) & kNibMask) | kMagic;
+  r.z = ((w >> 8) & kNibMask) | kMagic;
+  r.w = (__builtin_amdgcn_alignbit(w, w, 12) & kNibMask) | kMagic;
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// The same word -> 8 fp16 elements equal to the signed codes exactly: the
+// nibble widens to fp16 128 + n (exponent 2^7, mantissa bits 3..6) and one
+// packed fp16 subtraction of 136 per pair leaves code = n - 8, which is
+// exactly representable.  Used where the operand offset must not enter the
+// fp32 accumulation (attention).
+__device__ __forceinline__ f16x8 widen_word_exact_f16(uint32_t w) {
+  u32x4 r;
+  r.x = (w & kNibMask) | 0x58005800u;
+  r.y = ((w >> 4) & kNibMask) | 0x58005800u;
+  r.z = ((w >> 8) & kNibMask) | 0x58005800u;
+  r.w = (__builtin_amdgcn_alignbit(w, w, 12) & kNibMask) | 0x58005800u;
+  const f16x8 v = __builtin_bit_cast(f16x8, r);
+  return v - (f16x8)(_Float16)136.0f;
+}
+
+__device__ __forceinline__ uint32_t rotl_dev(uint32_t x, int r) {
+  r &= 31;
+  return r ? __builtin_amdgcn_alignbit(x, x, 32 - r) : x;
+}
+
+// element e of a word holding nibble n, other bits zero
+__device__ __forceinline__ uint32_t nibble_bits(int e, uint32_t n) {
+  return rotl_dev(n << 3, 4 * (e >> 1) + 16 * (e & 1));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
@@ -64,6 +96,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// An fp64 value as an unevaluated fp32 pair hi + lo.  Sums of bf16 operands
+// are formed exactly in fp64 and carried as such pairs, so that removing the
+// nibble offset (24 * sum) costs two fp32 FMAs and no precision.
+__device__ __forceinline__ float2 split_f64(double v) {
+  const float hi = (float)v;
+  return float2{hi, (float)(v - (double)hi)};
+}
+
+// d - 24 * (hi + lo) with one rounding per step
+__device__ __forceinline__ float remove_offset(float d, float2 s) {
+  return fmaf(-kBias, s.y, fmaf(-kBias, s.x, d));
 }
 
 }  // namespace futx

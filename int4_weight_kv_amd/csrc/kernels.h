@@ -37,14 +37,15 @@ AttnPlan attn_plan(int B, int nkv, int max_context);
 
 hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* act, float* invr,
                            hipStream_t st);
-hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float* gsum, hipStream_t st);
-hipError_t launch_gemm_partial(const void* wpk, const void* wsc, const uint16_t* act,
-                               const float* gsum, int B, int N, int K, int G, float* part,
-                               const GemmPlan& plan, hipStream_t st);
+hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float2* gsum, hipStream_t st);
+// act: nterms (1 or 3) bf16 activation terms [B][K], term t at act + t * term_stride
+hipError_t launch_gemm_partial(const void* wpk, const void* wsc, const uint16_t* act, int nterms,
+                               size_t term_stride, const float2* gsum, int B, int N, int K, int G,
+                               float* part, const GemmPlan& plan, hipStream_t st);
 hipError_t launch_reduce(const float* part, int S, int B, int N, const float* rowscale,
                          const float* resid, float* out, int gateup_inter, hipStream_t st);
 hipError_t launch_swiglu(const float* part, int S, int B, int I, int G, const float* invr,
-                         uint16_t* act, float* gsum, hipStream_t st);
+                         uint16_t* act, float2* gsum, hipStream_t st);
 hipError_t launch_kv_append(const float* k, const float* v, const int32_t* positions,
                             const int32_t* slots, int n, uint32_t flags, int D, int hb,
                             float theta, const KVPtrs& kv, hipStream_t st);
@@ -56,8 +57,10 @@ hipError_t launch_attention(const void* q, bool q_f32, const int32_t* lens, int 
                             const int32_t* block_table, int mpps, int B, int nq, int D,
                             const AttnPlan& plan, const KVPtrsConst& kv, float* apart,
                             hipStream_t st);
+// out_bf16: three bf16 terms of o, term t at out_bf16 + t * term_stride
 hipError_t launch_attn_merge(const float* apart, const int32_t* lens, int len_add, int B, int nq,
                              int D, const AttnPlan& plan, int hb, float* out_f32,
-                             uint16_t* out_bf16, float* gsum, int G, hipStream_t st);
+                             uint16_t* out_bf16, size_t term_stride, float2* gsum, int G,
+                             hipStream_t st);
 
 }  // namespace futx

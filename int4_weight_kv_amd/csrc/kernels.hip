@@ -38,14 +38,15 @@ __global__ __launch_bounds__(256) void prep_act_kernel(const float* __restrict__
   if (threadIdx.x == 0) invr[b] = 1.0f / sqrtf(red[0] / (float)H + eps);
 }
 
-// gsum[j * 32 + b] = sum of the bf16 values act[b][j*G .. j*G+G-1] (fp32).
+// gsum[j * 32 + b] = sum of the bf16 values act[b][j*G .. j*G+G-1], exact in
+// fp64, stored as an fp32 (hi, lo) pair.
 __global__ __launch_bounds__(64) void gsum_kernel(const uint16_t* __restrict__ act, int K, int G,
-                                                  float* __restrict__ gsum) {
+                                                  float2* __restrict__ gsum) {
   const int j = blockIdx.x, b = blockIdx.y;
-  float s = 0.f;
-  for (int c = threadIdx.x; c < G; c += 64) s += bf16_bits_to_f32(act[(size_t)b * K + (size_t)j * G + c]);
-  s = wave_sum(s);
-  if (threadIdx.x == 0) gsum[j * kMaxBatch + b] = s;
+  double s = 0.0;
+  for (int c = threadIdx.x; c < G; c += 64) s += (double)bf16_bits_to_f32(act[(size_t)b * K + (size_t)j * G + c]);
+  s = wave_sum_f64(s);
+  if (threadIdx.x == 0) gsum[j * kMaxBatch + b] = split_f64(s);
 }
 
 // ---------------------------------------------------------------- INT4 GEMM
@@ -53,14 +54,16 @@ __global__ __launch_bounds__(64) void gsum_kernel(const uint16_t* __restrict__ a
 // Split-K partial products of one packed projection.  One wave per
 // (16-row tile, K split); per K block it loads 16 bytes of nibbles per lane
 // (four MFMA steps), widens them to bf16 in registers and multiplies with
-// the bf16 activations.  Per weight group the MFMA sum is corrected for the
-// nibble offset with the activation group sum and scaled by the group scale.
+// the bf16 activations (NT = 3: an activation given as a sum of three bf16
+// terms, accumulated in the same fp32 sum).  Per weight group the MFMA sum is corrected for the
+// nibble offset with the exact activation group sum and scaled by the group
+// scale.
 // part[split][b][P] (fp32, physical row order).
-template <int G, int NF>
+template <int G, int NF, int NT>
 __global__ __launch_bounds__(256) void gemm_partial_kernel(
     const uint4* __restrict__ wpk, const uint16_t* __restrict__ wsc,
-    const uint16_t* __restrict__ act, const float* __restrict__ gsum, int B, int N, int K,
-    int kbps, int S, float* __restrict__ part) {
+    const uint16_t* __restrict__ act, size_t term_stride, const float2* __restrict__ gsum, int B,
+    int N, int K, int kbps, int S, float* __restrict__ part) {
   const int lane = threadIdx.x & 63;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int ntiles = N / 16;
@@ -76,17 +79,20 @@ __global__ __launch_bounds__(256) void gemm_partial_kernel(
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int kb = kb0; kb < kb1; ++kb) {
     const uint4 wv = wpk[((size_t)nt * KB + kb) * 64 + lane];
-    bf16x8 a[NF][4];
+    bf16x8 a[NT][NF][4];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int tok = f * 16 + col;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint4 av = {0u, 0u, 0u, 0u};
-        if (tok < B) av = *(const uint4*)(act + (size_t)tok * K + kb * 128 + s * 32 + grp * 8);
-        a[f][s] = as_bf16x8(av);
+      for (int f = 0; f < NF; ++f) {
+        const int tok = f * 16 + col;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint4 av = {0u, 0u, 0u, 0u};
+          if (tok < B)
+            av = *(const uint4*)(act + t * term_stride + (size_t)tok * K + kb * 128 + s * 32 + grp * 8);
+          a[t][f][s] = as_bf16x8(av);
+        }
       }
-    }
 #pragma unroll
     for (int gi = 0; gi < 128 / G; ++gi) {
       f32x4 d[NF];
@@ -97,7 +103,9 @@ __global__ __launch_bounds__(256) void gemm_partial_kernel(
         const int s = gi * (G / 32) + ss;
         const bf16x8 bw = widen_word(word_of(wv, s));
 #pragma unroll
-        for (int f = 0; f < NF; ++f) d[f] = mfma16(a[f][s], bw, d[f]);
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int f = 0; f < NF; ++f) d[f] = mfma16(a[t][f][s], bw, d[f]);
       }
       const int j = kb * (128 / G) + gi;
       const float sc = half_bits_to_f32(wsc[(size_t)n * ngroups + j]);
@@ -106,8 +114,8 @@ __global__ __launch_bounds__(256) void gemm_partial_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tok = f * 16 + 4 * grp + r;
-          const float gs = tok < B ? gsum[j * kMaxBatch + tok] : 0.f;
-          acc[f][r] += sc * (d[f][r] - kBias * gs);
+          const float2 gs = tok < B ? gsum[j * kMaxBatch + tok] : float2{0.f, 0.f};
+          acc[f][r] = fmaf(sc, remove_offset(d[f][r], gs), acc[f][r]);
         }
       }
     }
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 __global__ __launch_bounds__(128) void swiglu_kernel(const float* __restrict__ part, int S, int B,
                                                      int I, int G, const float* __restrict__ invr,
                                                      uint16_t* __restrict__ act,
-                                                     float* __restrict__ gsum) {
+                                                     float2* __restrict__ gsum) {
   const int c = blockIdx.x * G + threadIdx.x, b = blockIdx.y;
   const int N = 2 * I;
   const int Pg = 32 * (c >> 4) + (c & 15), Pu = Pg + 16;
@@ -165,11 +173,11 @@ __global__ __launch_bounds__(128) void swiglu_kernel(const float* __restrict__ p
   const float a = g / (1.0f + expf(-g)) * u;
   const uint16_t ab = f32_to_bf16_bits(a);
   act[(size_t)b * I + c] = ab;
-  float s = wave_sum(bf16_bits_to_f32(ab));
-  __shared__ float red[2];
+  const double s = wave_sum_f64((double)bf16_bits_to_f32(ab));
+  __shared__ double red[2];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) gsum[blockIdx.x * kMaxBatch + b] = G > 64 ? red[0] + red[1] : red[0];
+  if (threadIdx.x == 0) gsum[blockIdx.x * kMaxBatch + b] = split_f64(G > 64 ? red[0] + red[1] : red[0]);
 }
 
 // ---------------------------------------------------------------- KV append
@@ -238,8 +246,6 @@ __device__ __forceinline__ uint16_t quantize_lane(const float (&x)[D / 64], int 
   return __half_as_ushort(s16);
 }
 
-__device__ __forceinline__ int nibble_bit(int e) { return (e & 1) ? 16 + 4 * (e >> 1) : 4 * (e >> 1); }
-
 // Writes one rotated token of KV head h into its slot.
 template <int D>
 __device__ void store_token(const float (&kx)[D / 64], const float (&vx)[D / 64], int slot, int h,
@@ -254,7 +260,7 @@ __device__ void store_token(const float (&kx)[D / 64], const float (&vx)[D / 64]
   const int e = lane & 7, g = (lane & 31) >> 3;
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) {
-    uint32_t w = (uint32_t)(qk[j] + (int)kNibbleBias) << nibble_bit(e);
+    uint32_t w = nibble_bits(e, (uint32_t)(qk[j] + (int)kNibbleBias));
     w |= __shfl_xor(w, 1, 64);
     w |= __shfl_xor(w, 2, 64);
     w |= __shfl_xor(w, 4, 64);
@@ -269,15 +275,15 @@ __device__ void store_token(const float (&kx)[D / 64], const float (&vx)[D / 64]
   const int tb = off >> 5, tp = off & 31;
   const int gv = tp < 16 ? tp >> 2 : (tp - 16) >> 2;
   const int ev = tp < 16 ? (tp & 3) : 4 + ((tp - 16) & 3);
-  const int bit = nibble_bit(ev);
+  const uint32_t vmask = nibble_bits(ev, 15u);
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) {
     const int c = lane + 64 * j;
     const int cg = c >> 6, c4 = (c & 63) >> 4;
     uint32_t* p = (uint32_t*)(kv.v_codes + head_base + (size_t)(tb * (D / 64) + cg) * 1024 +
                               (size_t)(gv * 16 + (c & 15)) * 16 + c4 * 4);
-    atomicAnd(p, ~(0xFu << bit));
-    atomicOr(p, (uint32_t)(qv[j] + (int)kNibbleBias) << bit);
+    atomicAnd(p, ~vmask);
+    atomicOr(p, nibble_bits(ev, (uint32_t)(qv[j] + (int)kNibbleBias)));
   }
   if (lane == 0) {
     kv.k_scales[((size_t)page * kv.nkv + h) * kPageSize + off] = sk;
@@ -356,16 +362,30 @@ __global__ __launch_bounds__(64) void post_qkv_kernel(const float* __restrict__ 
 //         lane L, reg r at 4 (L/16) + r.
 //   p.v:  A = probabilities (heads x 32 tokens) built directly from the two
 //         score tiles of a 32-token block, B = value tile.
-// Both fp32 operands (the query and p * value scale) enter the bf16 MFMA as
-// a hi + lo pair of bf16 values, so the products keep about 16 significant
-// bits instead of 8.  Nibble offsets are removed with the operand sums.
+// Precision: the attention output feeds a bf16 rounding point (the O
+// projection operand), so it is kept at fp32 accuracy.  Keys and values
+// widen to their exact signed codes in fp16 (no offset term in the fp32
+// accumulators), and the two fp32 operands (query, p * value scale) enter
+// the fp16 MFMA as a hi + lo pair (22 significant bits) after an exact
+// power-of-two scaling into fp16 range.
 // apart[((b * nq + i) * nsplit + sp) * (D + 2)] = {m, l, acc[0..D)}.
-__device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo) {
-  *hi = f32_to_bf16_bits(x);
-  *lo = f32_to_bf16_bits(x - bf16_bits_to_f32(*hi));
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-__device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) { return (uint32_t)a | ((uint32_t)b << 16); }
+// x (already scaled into fp16 range) -> fp16 hi + lo
+__device__ __forceinline__ void split_f16(float x, _Float16* hi, _Float16* lo) {
+  *hi = (_Float16)x;
+  *lo = (_Float16)(x - (float)*hi);
+}
+
+// power-of-two exponent k such that m * 2^k lies in [2^(top-1), 2^top)
+__device__ __forceinline__ int range_exp(float m, int top) {
+  if (!(m > 0.f)) return 0;
+  int e;
+  (void)frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
+  return top - e;
+}
 
 template <int D, bool QF32>
 __global__ __launch_bounds__(64) void attn_split_kernel(
@@ -379,49 +399,60 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   if (t0 >= t1) return;
   const int col = lane & 15, grp = lane >> 4;
   // query fragments (B operand): column = query head h*G + col
-  bf16x8 qh[D / 32], ql[D / 32];
-  float qs = 0.f;
+  f16x8 qh[D / 32], ql[D / 32];
+  float qscale;  // 2^-kq of this lane's head
   {
     const bool ok = col < G;
     const size_t qoff = ((size_t)b * nq + h * G + col) * D;
+    float qv[D / 32][8];
+    float qmax = 0.f;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      uint32_t hw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[s][e] = 0.f;
       if (ok) {
         if constexpr (QF32) {
           const float4* qp = (const float4*)((const float*)qin + qoff + s * 32 + grp * 8);
           const float4 a = qp[0], c = qp[1];
-          const float f[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            uint16_t h0, l0, h1, l1;
-            split_bf16(f[e], &h0, &l0);
-            split_bf16(f[e + 1], &h1, &l1);
-            hw[e / 2] = pack2(h0, h1);
-            lw[e / 2] = pack2(l0, l1);
-            qs += (bf16_bits_to_f32(h0) + bf16_bits_to_f32(l0)) + (bf16_bits_to_f32(h1) + bf16_bits_to_f32(l1));
-          }
+          qv[s][0] = a.x; qv[s][1] = a.y; qv[s][2] = a.z; qv[s][3] = a.w;
+          qv[s][4] = c.x; qv[s][5] = c.y; qv[s][6] = c.z; qv[s][7] = c.w;
         } else {
           const uint4 v = *(const uint4*)((const uint16_t*)qin + qoff + s * 32 + grp * 8);
-          hw[0] = v.x; hw[1] = v.y; hw[2] = v.z; hw[3] = v.w;
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            qs += bf16_bits_to_f32(hw[e] & 0xFFFF) + bf16_bits_to_f32(hw[e] >> 16);
+          for (int e = 0; e < 4; ++e) {
+            qv[s][2 * e] = bf16_bits_to_f32(w[e] & 0xFFFF);
+            qv[s][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
+          }
         }
       }
-      qh[s] = as_bf16x8(uint4{hw[0], hw[1], hw[2], hw[3]});
-      ql[s] = as_bf16x8(uint4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qv[s][e]));
+    }
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+    const int kq = range_exp(qmax, 11);
+    qscale = ldexpf(1.0f, -kq);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        _Float16 h0, l0, h1, l1;
+        split_f16(ldexpf(qv[s][e], kq), &h0, &l0);
+        split_f16(ldexpf(qv[s][e + 1], kq), &h1, &l1);
+        hw[e / 2] = pack_h2(h0, h1);
+        lw[e / 2] = pack_h2(l0, l1);
+      }
+      qh[s] = __builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+      ql[s] = __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
     }
   }
-  qs += __shfl_xor(qs, 16, 64);
-  qs += __shfl_xor(qs, 32, 64);
-  const float qbias = kBias * qs;  // per head col: 136 * sum of the query operand
+  const float zscale = qscale * scale;
   float m_i = -INFINITY, l_part = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
-  const bf16x8 ones = as_bf16x8(uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const size_t head_bytes = (size_t)kPageSize * D / 2;
   for (int blk = t0; blk < t1; blk += 32) {
     const int page = block_table[(size_t)b * mpps + blk / kPageSize];
@@ -463,14 +494,15 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        const bf16x8 kb = widen_word(kw[u][s]);
-        d = mfma16(kb, qh[s], d);
-        if constexpr (QF32) d = mfma16(kb, ql[s], d);
+        const f16x8 kc = widen_word_exact_f16(kw[u][s]);
+        d = mfma16h(kc, qh[s], d);
+        d = mfma16h(kc, ql[s], d);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = blk + 16 * u + 4 * grp + r;
-        z[u][r] = t < t1 ? (d[r] - qbias) * ks[u][r] * scale : -INFINITY;
+        z[u][r] = t < t1 ? d[r] * ks[u][r] * zscale : -INFINITY;
+        if (t >= t1) vs[u][r] = 0.f;  // stale scales past the end stay out of p.v
         mloc = fmaxf(mloc, z[u][r]);
       }
     }
@@ -478,43 +510,46 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     const float m_new = fmaxf(m_i, mloc);
     const float alpha = expf(m_i - m_new);
+    // exact power-of-two scaling of p * vs (<= max vs) into fp16 range
+    float vmax = fmaxf(fmaxf(fmaxf(vs[0][0], vs[0][1]), fmaxf(vs[0][2], vs[0][3])),
+                       fmaxf(fmaxf(vs[1][0], vs[1][1]), fmaxf(vs[1][2], vs[1][3])));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 16, 64));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 32, 64));
+    const int kp = range_exp(vmax, 14);
     float psum = 0.f;
-    uint16_t ph[8], pl[8];
+    uint32_t phw[4], plw[4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = expf(z[u][r] - m_new);
-        psum += p;
-        // tokens past the end may hold stale scales: keep them out of p.v
-        const float pv = z[u][r] == -INFINITY ? 0.f : p * vs[u][r];
-        split_bf16(pv, &ph[4 * u + r], &pl[4 * u + r]);
+      for (int r = 0; r < 4; r += 2) {
+        const float p0 = expf(z[u][r] - m_new), p1 = expf(z[u][r + 1] - m_new);
+        psum += p0 + p1;
+        _Float16 h0, l0, h1, l1;
+        split_f16(ldexpf(p0 * vs[u][r], kp), &h0, &l0);
+        split_f16(ldexpf(p1 * vs[u][r + 1], kp), &h1, &l1);
+        phw[2 * u + r / 2] = pack_h2(h0, h1);
+        plw[2 * u + r / 2] = pack_h2(l0, l1);
       }
     }
     l_part = l_part * alpha + psum;
     m_i = m_new;
-    const bf16x8 pah = as_bf16x8(uint4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])});
-    const bf16x8 pal = as_bf16x8(uint4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])});
+    const f16x8 pah = __builtin_bit_cast(f16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
+    const f16x8 pal = __builtin_bit_cast(f16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
     // rescale the p.v accumulators: row 4 (L/16) + r belongs to head 4 grp + r
     float al[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[c][r] *= al[r];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc1[r] *= al[r];
+    const float pback = ldexpf(1.0f, -kp);
 #pragma unroll
     for (int cg = 0; cg < D / 64; ++cg)
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        const bf16x8 vb = widen_word(word_of(vw[cg], c4));
-        acc[cg * 4 + c4] = mfma16(pah, vb, acc[cg * 4 + c4]);
-        acc[cg * 4 + c4] = mfma16(pal, vb, acc[cg * 4 + c4]);
+        const f16x8 vc = widen_word_exact_f16(word_of(vw[cg], c4));
+        f32x4 dv = mfma16h(pah, vc, f32x4{0.f, 0.f, 0.f, 0.f});
+        dv = mfma16h(pal, vc, dv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
       }
-    acc1 = mfma16(pah, ones, acc1);
-    acc1 = mfma16(pal, ones, acc1);
   }
   // finalize this chunk's partials
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
@@ -534,20 +569,24 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const int c = cg * 64 + c4 * 16 + col;
-          out[i * head_stride + 2 + c] = acc[cg * 4 + c4][r] - kBias * acc1[r];
+          out[i * head_stride + 2 + c] = acc[cg * 4 + c4][r];
         }
     }
   }
 }
 
 // Merge of the split partials + inverse block Hadamard.  One block of D
-// threads per (query head, sequence).  Writes fp32 output, or bf16 output
-// plus the group sums of the O projection input.
+// threads per (query head, sequence).  Writes fp32 output, or the operand of
+// the O projection: o as an unevaluated sum of three bf16 terms
+// (hi + mid + lo, 24 significant bits, term t at out_bf16 + t * term_stride)
+// plus the exact group sums of that sum.  The attention output comes out of
+// a long fp32 reduction, so a single bf16 rounding here would flip on tiny
+// differences; three terms carry it at fp32 accuracy.
 template <int D>
 __global__ __launch_bounds__(128) void attn_merge_kernel(
     const float* __restrict__ apart, const int32_t* __restrict__ lens, int len_add, int nq,
     int chunk, int nsplit, int hb, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
-    float* __restrict__ gsum, int G) {
+    size_t term_stride, float2* __restrict__ gsum, int G) {
   const int i = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int L = lens[b] + len_add;
   const int nsp = (L + chunk - 1) / chunk;
@@ -560,29 +599,36 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(
     l += w * base[sp * (D + 2) + 1];
     a += w * base[sp * (D + 2) + 2 + c];
   }
-  float o[1] = {l > 0.f ? a / l : 0.f};
+  float o = l > 0.f ? a / l : 0.f;
   // inverse rotation (the normalized Sylvester matrix is its own inverse)
   const int lane = c & 63;
   for (int hop = 1; hop < hb; hop <<= 1) {
-    const float p = __shfl_xor(o[0], hop, 64);
-    o[0] = (lane & hop) ? p - o[0] : o[0] + p;
+    const float p = __shfl_xor(o, hop, 64);
+    o = (lane & hop) ? p - o : o + p;
   }
-  o[0] *= 1.0f / sqrtf((float)hb);
-  if (out_f32) out_f32[((size_t)b * nq + i) * D + c] = o[0];
+  o *= 1.0f / sqrtf((float)hb);
+  if (out_f32) out_f32[((size_t)b * nq + i) * D + c] = o;
   if (out_bf16) {
-    const uint16_t ob = f32_to_bf16_bits(o[0]);
-    out_bf16[(size_t)b * nq * D + (size_t)i * D + c] = ob;
-    // group sums: groups of G (64 or 128) channels inside the head
-    float s = wave_sum(bf16_bits_to_f32(ob));
-    __shared__ float red[2];
+    const uint16_t t0 = f32_to_bf16_bits(o);
+    const float r1 = o - bf16_bits_to_f32(t0);
+    const uint16_t t1 = f32_to_bf16_bits(r1);
+    const uint16_t t2 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(t1));
+    const size_t at = (size_t)b * nq * D + (size_t)i * D + c;
+    out_bf16[at] = t0;
+    out_bf16[at + term_stride] = t1;
+    out_bf16[at + 2 * term_stride] = t2;
+    // group sums (groups of G = 64 or 128 channels inside the head)
+    const double s = wave_sum_f64((double)bf16_bits_to_f32(t0) + (double)bf16_bits_to_f32(t1) +
+                                  (double)bf16_bits_to_f32(t2));
+    __shared__ double red[2];
     if (lane == 0) red[c >> 6] = s;
     __syncthreads();
     if (c == 0) {
       const int gpr = D / G;  // groups per head
       for (int g2 = 0; g2 < gpr; ++g2) {
-        float t = 0.f;
+        double t = 0.0;
         for (int w = g2 * (G / 64); w < (g2 + 1) * (G / 64); ++w) t += red[w];
-        gsum[(size_t)(i * gpr + g2) * kMaxBatch + b] = t;
+        gsum[(size_t)(i * gpr + g2) * kMaxBatch + b] = split_f64(t);
       }
     }
   }
@@ -603,7 +649,7 @@ hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* ac
   return hipSuccess;
 }
 
-hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float* gsum, hipStream_t st) {
+hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float2* gsum, hipStream_t st) {
   gsum_kernel<<<dim3(K / G, B), 64, 0, st>>>(act, K, G, gsum);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
@@ -621,24 +667,29 @@ GemmPlan gemm_plan(int N, int K) {
   return p;
 }
 
-hipError_t launch_gemm_partial(const void* wpk, const void* wsc, const uint16_t* act,
-                               const float* gsum, int B, int N, int K, int G, float* part,
-                               const GemmPlan& plan, hipStream_t st) {
+hipError_t launch_gemm_partial(const void* wpk, const void* wsc, const uint16_t* act, int nterms,
+                               size_t term_stride, const float2* gsum, int B, int N, int K, int G,
+                               float* part, const GemmPlan& plan, hipStream_t st) {
   const int waves = (N / 16) * plan.splits;
   const dim3 grid((waves + 3) / 4), block(256);
   const uint4* w = (const uint4*)wpk;
   const uint16_t* s = (const uint16_t*)wsc;
-  if (G == 128) {
-    if (B <= 16)
-      gemm_partial_kernel<128, 1><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
-    else
-      gemm_partial_kernel<128, 2><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
+#define FUTX_GEMM(GG, NF, NT) \
+  gemm_partial_kernel<GG, NF, NT><<<grid, block, 0, st>>>(w, s, act, term_stride, gsum, B, N, K, plan.kbps, plan.splits, part)
+  if (nterms == 3) {
+    if (G == 128) {
+      if (B <= 16) FUTX_GEMM(128, 1, 3); else FUTX_GEMM(128, 2, 3);
+    } else {
+      if (B <= 16) FUTX_GEMM(64, 1, 3); else FUTX_GEMM(64, 2, 3);
+    }
   } else {
-    if (B <= 16)
-      gemm_partial_kernel<64, 1><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
-    else
-      gemm_partial_kernel<64, 2><<<grid, block, 0, st>>>(w, s, act, gsum, B, N, K, plan.kbps, plan.splits, part);
+    if (G == 128) {
+      if (B <= 16) FUTX_GEMM(128, 1, 1); else FUTX_GEMM(128, 2, 1);
+    } else {
+      if (B <= 16) FUTX_GEMM(64, 1, 1); else FUTX_GEMM(64, 2, 1);
+    }
   }
+#undef FUTX_GEMM
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -652,7 +703,7 @@ hipError_t launch_reduce(const float* part, int S, int B, int N, const float* ro
 }
 
 hipError_t launch_swiglu(const float* part, int S, int B, int I, int G, const float* invr,
-                         uint16_t* act, float* gsum, hipStream_t st) {
+                         uint16_t* act, float2* gsum, hipStream_t st) {
   swiglu_kernel<<<dim3(I / G, B), G, 0, st>>>(part, S, B, I, G, invr, act, gsum);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
@@ -715,12 +766,13 @@ hipError_t launch_attention(const void* q, bool q_f32, const int32_t* lens, int 
 
 hipError_t launch_attn_merge(const float* apart, const int32_t* lens, int len_add, int B, int nq,
                              int D, const AttnPlan& plan, int hb, float* out_f32,
-                             uint16_t* out_bf16, float* gsum, int G, hipStream_t st) {
+                             uint16_t* out_bf16, size_t term_stride, float2* gsum, int G,
+                             hipStream_t st) {
   const dim3 grid(nq, B);
   if (D == 128)
-    attn_merge_kernel<128><<<grid, 128, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, gsum, G);
+    attn_merge_kernel<128><<<grid, 128, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride, gsum, G);
   else
-    attn_merge_kernel<64><<<grid, 64, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, gsum, G);
+    attn_merge_kernel<64><<<grid, 64, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride, gsum, G);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }

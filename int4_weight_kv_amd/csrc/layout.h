@@ -13,14 +13,17 @@
 // directly into MMA operands").
 //
 // Nibble encoding inside a 32-bit word: a word carries operand elements
-// e = 0..7 of one lane and one MFMA step; element 2j sits in bits 4j..4j+3
-// and element 2j+1 in bits 16+4j..16+4j+3, each as (code + 8).  Then
-//   ((w >> 4j) & 0x000F000F) | 0x43004300
-// is a pair of bf16 values (128 + code + 8) for elements 2j, 2j+1: two
-// elements per two ALU instructions, no conversion instruction.  The
-// constant offset 136 is removed after the MFMA with the group sums of the
-// other operand: sum_k (136 + q_k) a_k = sum_k q_k a_k + 136 sum_k a_k.
-//
+// e = 0..7 of one lane and one MFMA step.  Element e is stored as
+// n = code + 8 in bits 3..6 rotated left by r(e) = 4 (e / 2) + 16 (e % 2)
+// (so element 7 wraps around bit 31).  For the element pair j = (2j, 2j+1),
+//   (rotr(w, 4j) & 0x00780078) | 0x41804180
+// is a pair of bf16 values 16 + n = 24 + code (exponent 2^4, the nibble in
+// mantissa bits 3..6): two elements per two ALU instructions (one for
+// j = 0), no conversion instruction.  The constant 24 is removed after the
+// MFMA with the sums of the other operand:
+//   sum_k (24 + q_k) a_k = sum_k q_k a_k + 24 sum_k a_k.
+// The offset is kept small (24 rather than 136 for a nibble in the low
+// mantissa bits) because the fp32 rounding of the MFMA sum scales with it.
 // Weights (one projection, N physical rows x K inputs, group G along K):
 //   packed[nt][kb][L][16 bytes], nt = row tile (16 rows), kb = K block (128),
 //   word s (bytes 4s..4s+3) of lane L holds row nt*16 + L%16 and inputs
@@ -60,14 +63,26 @@ inline size_t weight_tile_offset(int nt, int kb, int kblocks) {
   return ((size_t)nt * kblocks + kb) * kTileBytes;
 }
 
-// byte offset and bit position of (physical row P, input k) in packed weights
-inline void weight_nibble_pos(int P, int k, int kblocks, size_t* byte_off, int* bit) {
+inline uint32_t rotl32(uint32_t x, int r) {
+  r &= 31;
+  return r ? (x << r) | (x >> (32 - r)) : x;
+}
+inline int nibble_rot(int e) { return 4 * (e >> 1) + 16 * (e & 1); }
+// word with element e set to nibble n (0..15)
+inline uint32_t nibble_put(uint32_t w, int e, uint32_t n) {
+  const int r = nibble_rot(e);
+  return (w & ~rotl32(0x78u, r)) | rotl32((n & 15u) << 3, r);
+}
+inline uint32_t nibble_get(uint32_t w, int e) { return (rotl32(w, 32 - nibble_rot(e)) >> 3) & 15u; }
+
+// byte offset of the word and element index of (physical row P, input k)
+inline void weight_nibble_pos(int P, int k, int kblocks, size_t* word_off, int* elem) {
   int nt = P / kTileN, i = P % kTileN;
   int kb = k / kTileK, kk = k % kTileK;
   int s = kk / 32, g = (kk % 32) / 8, e = kk % 8;
   int lane = g * 16 + i;
-  *byte_off = weight_tile_offset(nt, kb, kblocks) + (size_t)lane * 16 + (size_t)s * 4;
-  *bit = (e & 1) ? 16 + 4 * (e >> 1) : 4 * (e >> 1);
+  *word_off = weight_tile_offset(nt, kb, kblocks) + (size_t)lane * 16 + (size_t)s * 4;
+  *elem = e;
 }
 
 // GATEUP: physical row of logical row n (0..2I-1); identity for the others.

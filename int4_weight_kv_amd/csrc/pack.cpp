@@ -97,11 +97,11 @@ bool pack_rows(const PackJob& j, int r0, int r1) {
     }
     for (int c = 0; c < j.k; ++c) {
       size_t off;
-      int bit;
-      weight_nibble_pos(P, c, j.kblocks, &off, &bit);
+      int e;
+      weight_nibble_pos(P, c, j.kblocks, &off, &e);
       uint32_t word;
       std::memcpy(&word, j.packed + off, 4);
-      word = (word & ~(0xFu << bit)) | ((uint32_t)(q[c] + (int)kNibbleBias) << bit);
+      word = nibble_put(word, e, (uint32_t)(q[c] + (int)kNibbleBias));
       std::memcpy(j.packed + off, &word, 4);
     }
   }
@@ -155,11 +155,11 @@ futx_status unpack_host(const futx_dims* dims, futx_proj proj, const void* packe
       uint8_t nib[2];
       for (int t = 0; t < 2; ++t) {
         size_t off;
-        int bit;
-        weight_nibble_pos(P, c + t, kblocks, &off, &bit);
+        int e;
+        weight_nibble_pos(P, c + t, kblocks, &off, &e);
         uint32_t word;
         std::memcpy(&word, pk + off, 4);
-        int code = (int)((word >> bit) & 0xF) - (int)kNibbleBias;
+        int code = (int)nibble_get(word, e) - (int)kNibbleBias;
         nib[t] = (uint8_t)(code & 0xF);
       }
       canon[(size_t)n * (ps.k / 2) + c / 2] = (uint8_t)(nib[0] | (nib[1] << 4));

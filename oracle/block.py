@@ -16,7 +16,10 @@ quant, hadamard, rope and attention):
       append at slot L_b.
   O9  attention over tokens 0..L_b of the cache (the new token read back
       quantized), inverse rotation of the output.
-  O10 h = x + W_o bf16(o)                                  (R2)
+  O10 h = x + W_o o  (o unrounded: the GPU carries the attention output
+      into the O projection as a sum of three bf16 terms, about fp32
+      accuracy, so there is no bf16 rounding point between attention and
+      the O projection)
   O11 RMSNorm-2 like O4: u2 = bf16(h), r2 = sqrt(mean(h^2) + eps)     (R3)
   O12 g = (W_gate u2)/r2, v = (W_up u2)/r2, act = bf16(silu(g) v)    (R4)
   O13 y = h + W_down act  -- the block output (fp64 here).
@@ -26,7 +29,9 @@ quant, hadamard, rope and attention):
       (W_head' u) / r with W_head' = bf16(fp32(W_head * final gain)); top-1 is
       the lowest index of the maximum.
 
-Everything is fp64 except the quantizers (fp32 recipe) and R1-R5.
+Everything is fp64 except the quantizers (fp32 recipe) and the bf16
+rounding points R1 (block input), R3 (MLP input), R4 (SwiGLU output) and R5
+(LM-head input), where the GPU materializes bf16 matrix-core operands.
 
 Parity status: the parts are pinned in tests/test_oracle_*.py; the composed
 block is checked against ``decode_block_unquantized`` (differences of
@@ -196,9 +201,9 @@ def decode_block(x, weights, caches, lens, dims, diag=None):
         k_hat, v_hat = caches[b].dequant(pos + 1)
         o[b] = decode_attention(q_rot, k_hat, v_hat, dims.had_block)
         q_rot_all[b] = q_rot
-    # O10
-    o_bf = bf16_round(o.reshape(bsz, nq * d))
-    h = x + o_bf @ weights.dense("o").T
+    # O10 (no rounding point: see the module docstring)
+    o_flat = o.reshape(bsz, nq * d)
+    h = x + o_flat @ weights.dense("o").T
     # O11 / O12
     u2 = bf16_round(h)
     r2 = rmsnorm_stats(h, dims.rms_eps)
@@ -208,7 +213,7 @@ def decode_block(x, weights, caches, lens, dims, diag=None):
     # O13
     y = h + act @ weights.dense("down").T
     if diag is not None:
-        diag.update(u=u, r=r, qkv=qkv, q_rot=q_rot_all, o=o, o_bf=o_bf, h=h, u2=u2, r2=r2, g=g, up=up, act=act)
+        diag.update(u=u, r=r, qkv=qkv, q_rot=q_rot_all, o=o, h=h, u2=u2, r2=r2, g=g, up=up, act=act)
     return y
 
 

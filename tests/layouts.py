@@ -3,8 +3,9 @@ description, independent of the library and of the oracle).
 
 Weights: packed[nt][kb][L][16 bytes]; word s (bytes 4s..4s+3, little endian)
 of lane L holds row nt*16 + L%16, inputs kb*128 + 32 s + 8 (L // 16) + e;
-element e = 2j sits in bits 4j..4j+3, e = 2j+1 in bits 16+4j..16+4j+3, each
-as code + 8.  GATEUP physical tile 2t = gate rows 16t.., 2t+1 = up rows 16t..
+element e is stored as code + 8 in bits 3..6 of the word rotated left by
+4 (e // 2) + 16 (e % 2).  GATEUP physical tile 2t = gate rows 16t..,
+2t+1 = up rows 16t..
 
 KV cache per (page, KV head): keys [tt][L][D/8 bytes] with token tt*16 + L%16
 and word s = channels 32 s + 8 (L//16) + e; values [tb][cg][L][16 bytes] with
@@ -17,10 +18,12 @@ import numpy as np
 
 def _nibbles(words):
     """uint32 [...] -> codes int8 [..., 8] in element order e = 0..7."""
+    w = np.asarray(words, np.uint64)
     out = np.empty(words.shape + (8,), np.int8)
     for e in range(8):
-        bit = 16 + 4 * (e // 2) if e % 2 else 4 * (e // 2)
-        out[..., e] = ((words >> np.uint32(bit)) & np.uint32(15)).astype(np.int16) - 8
+        r = 4 * (e // 2) + 16 * (e % 2)
+        rot = ((w >> np.uint64(r)) | (w << np.uint64(32 - r))) & np.uint64(0xFFFFFFFF) if r else w
+        out[..., e] = ((rot >> np.uint64(3)) & np.uint64(15)).astype(np.int16) - 8
     return out
 
 

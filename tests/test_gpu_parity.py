@@ -189,6 +189,7 @@ def test_int4_linear(F, DB, shape, batch):
         q, s = oracle.quantize_weight_rtn(folded, d.w_group)
         ref = act.astype(np.float64) @ oracle.dequant_weight(q, s, d.w_group).T
         err = np.max(np.abs(out.cpu().numpy() - ref))
+        say("  max err %.3g  (max|ref| %.3g)" % (err, np.max(np.abs(ref))))
         # fp32 accumulation over K inputs: far below the block tolerance
         assert err <= 1e-5 * np.max(np.abs(ref)) * np.sqrt(kk / 128) + 1e-6, (proj, err)
 
