@@ -6,6 +6,7 @@
 #include <cstring>
 #include <vector>
 
+#include "gemm.h"
 #include "internal.h"
 #include "kernels.h"
 
@@ -60,6 +61,7 @@ futx_status check_dims(const futx_dims* d) {
   for (int k : ks)
     if (k % kTileK || k % d->w_group) return fail(FUTX_E_UNSUPPORTED, "projection inputs must be multiples of 128");
   if (d->hidden % kTileN || d->intermediate % kTileN) return fail(FUTX_E_UNSUPPORTED, "bad row count");
+
   return FUTX_OK;
 }
 
@@ -94,7 +96,7 @@ static size_t part_floats(const futx_dims& d, int B) {
   size_t m = 0;
   for (int p = 0; p < 4; ++p) {
     ProjShape s = proj_shape(d, (futx_proj)p);
-    GemmPlan g = gemm_plan(s.n, s.k);
+    GemmPlan2 g = plan_gemm(s.n, s.k, d.w_group, B, p == FUTX_PROJ_O ? 3 : 1, kEpiPartial);
     size_t v = (size_t)g.splits * B * s.n;
     if (v > m) m = v;
   }
@@ -278,20 +280,54 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
   const int nqkv = (d.n_heads + 2 * d.n_kv_heads) * D, I = d.intermediate;
   const KVPtrs kv = kv_ptrs(cache, d.n_kv_heads);
   const KVPtrsConst kvc = kv_cptrs(cache, d.n_kv_heads);
+  const size_t term = (size_t)kMaxBatch * kmax(d);
   hipError_t e;
 #define STEP(call)                                             \
   do {                                                         \
     if ((e = (call)) != hipSuccess) return hip_fail(e, #call); \
   } while (0)
-  // RMSNorm-1 operand and 1/r
-  STEP(launch_prep_act(x, B, H, d.rms_eps, ws.act, ws.invr, s));
-  STEP(launch_gsum(ws.act, B, H, G, ws.gsum, s));
-  // QKV
-  GemmPlan gq = gemm_plan(nqkv, H);
-  const size_t term = (size_t)kMaxBatch * kmax(d);
-  STEP(launch_gemm_partial(w->qkv.packed, w->qkv.scales, ws.act, 1, term, ws.gsum, B, nqkv, H, G, ws.part, gq, s));
-  STEP(launch_reduce(ws.part, gq.splits, B, nqkv, ws.invr, nullptr, ws.qkv, 0, s));
-  // RoPE, rotation, INT4 append of the new token; rotated bf16 queries
+  // One INT4 projection with its fused epilogue.  When the activation range
+  // does not fit in LDS for this batch, K is split (partial sums) and the
+  // epilogue runs as separate kernels.
+  auto gemm = [&](const futx_qweight& q, int N, int K, const void* act, int nterms, bool f32, int epi,
+                  const float* resid, float* out, uint16_t* out_bf16) -> hipError_t {
+    GemmArgs a{};
+    a.w = (const uint4*)q.packed;
+    a.sc = (const uint16_t*)q.scales;
+    a.act = act;
+    a.term_stride = term;
+    a.N = N;
+    a.K = K;
+    a.B = B;
+    a.eps = d.rms_eps;
+    a.resid = resid;
+    a.out = out;
+    a.out_bf16 = out_bf16;
+    a.inter = I;
+    if (gemm_fits(K, G, B, nterms, epi)) {
+      apply_plan(a, plan_gemm(N, K, G, B, nterms, epi));
+      return launch_int4_gemm(a, G, nterms, f32, epi, s);
+    }
+    const GemmPlan2 p = plan_gemm(N, K, G, B, nterms, kEpiPartial);
+    apply_plan(a, p);
+    a.out = ws.part;
+    hipError_t e2 = launch_int4_gemm(a, G, nterms, f32, kEpiPartial, s);
+    if (e2 != hipSuccess) return e2;
+    switch (epi) {
+      case kEpiRms:
+        if ((e2 = launch_prep_act((const float*)act, B, K, d.rms_eps, ws.act, ws.invr, s)) != hipSuccess) return e2;
+        return launch_reduce(ws.part, p.splits, B, N, ws.invr, nullptr, out, 0, s);
+      case kEpiResid:
+        return launch_reduce(ws.part, p.splits, B, N, nullptr, resid, out, 0, s);
+      case kEpiSwiglu:
+        if ((e2 = launch_prep_act((const float*)act, B, K, d.rms_eps, ws.act, ws.invr2, s)) != hipSuccess) return e2;
+        return launch_swiglu(ws.part, p.splits, B, I, G, ws.invr2, out_bf16, ws.gsum, s);
+    }
+    return hipErrorInvalidValue;
+  };
+  // RMSNorm-1 + QKV (the gain is folded into the weights; 1/r in the epilogue)
+  STEP(gemm(w->qkv, nqkv, H, x, 1, true, kEpiRms, nullptr, ws.qkv, nullptr));
+  // RoPE, rotation, INT4 append of the new token; rotated fp32 queries
   STEP(launch_post_qkv(ws.qkv, B, nq, D, cached_lens, block_table, max_pages_per_seq, d.had_block,
                        d.rope_theta, ws.qrot, kv, s));
   // attention over positions 0..cached_lens[b]
@@ -299,21 +335,13 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
   STEP(launch_attention(ws.qrot, true, cached_lens, 1, block_table, max_pages_per_seq, B, nq, D,
                         ap, kvc, ws.apart, s));
   STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act,
-                         term, ws.gsum, G, s));
-  // O projection + residual
-  GemmPlan go = gemm_plan(H, nq * D);
-  STEP(launch_gemm_partial(w->o.packed, w->o.scales, ws.act, 3, term, ws.gsum, B, H, nq * D, G, ws.part, go, s));
-  STEP(launch_reduce(ws.part, go.splits, B, H, nullptr, x, ws.h, 0, s));
-  // RMSNorm-2 operand, gate/up + SwiGLU
-  STEP(launch_prep_act(ws.h, B, H, d.rms_eps, ws.act, ws.invr2, s));
-  STEP(launch_gsum(ws.act, B, H, G, ws.gsum, s));
-  GemmPlan gg = gemm_plan(2 * I, H);
-  STEP(launch_gemm_partial(w->gateup.packed, w->gateup.scales, ws.act, 1, term, ws.gsum, B, 2 * I, H, G, ws.part, gg, s));
-  STEP(launch_swiglu(ws.part, gg.splits, B, I, G, ws.invr2, ws.act, ws.gsum, s));
-  // down projection + residual
-  GemmPlan gd = gemm_plan(H, I);
-  STEP(launch_gemm_partial(w->down.packed, w->down.scales, ws.act, 1, term, ws.gsum, B, H, I, G, ws.part, gd, s));
-  STEP(launch_reduce(ws.part, gd.splits, B, H, nullptr, ws.h, x, 0, s));
+                         term, nullptr, G, s));
+  // O projection + residual: h = x + O(o)
+  STEP(gemm(w->o, H, nq * D, ws.act, 3, false, kEpiResid, x, ws.h, nullptr));
+  // RMSNorm-2 + gate/up + SwiGLU -> bf16 activation
+  STEP(gemm(w->gateup, 2 * I, H, ws.h, 1, true, kEpiSwiglu, nullptr, nullptr, ws.act));
+  // down projection + residual: x = h + down(act)
+  STEP(gemm(w->down, H, I, ws.act, 1, false, kEpiResid, ws.h, x, nullptr));
 #undef STEP
   return FUTX_OK;
 }
@@ -331,15 +359,21 @@ futx_status futx_int4_linear(const futx_dims* dims, futx_proj proj, const futx_q
     return fail(FUTX_E_WORKSPACE, "int4_linear: workspace %zu < %zu bytes", workspace_bytes, ws.bytes);
   ProjShape ps = proj_shape(*dims, proj);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  GemmPlan g = gemm_plan(ps.n, ps.k);
-  if ((e = launch_gsum(act, batch, ps.k, dims->w_group, ws.gsum, s)) != hipSuccess) return hip_fail(e, "gsum");
-  if ((e = launch_gemm_partial(w->packed, w->scales, act, 1, 0, ws.gsum, batch, ps.n, ps.k, dims->w_group,
-                               ws.part, g, s)) != hipSuccess)
-    return hip_fail(e, "gemm");
-  if ((e = launch_reduce(ws.part, g.splits, batch, ps.n, nullptr, nullptr, out,
-                         proj == FUTX_PROJ_GATEUP ? dims->intermediate : 0, s)) != hipSuccess)
-    return hip_fail(e, "reduce");
+  GemmArgs a{};
+  a.w = (const uint4*)w->packed;
+  a.sc = (const uint16_t*)w->scales;
+  a.act = act;
+  a.N = ps.n;
+  a.K = ps.k;
+  a.B = batch;
+  a.out = ws.part;
+  const GemmPlan2 p = plan_gemm(ps.n, ps.k, dims->w_group, batch, 1, kEpiPartial);
+  apply_plan(a, p);
+  hipError_t e = launch_int4_gemm(a, dims->w_group, 1, false, kEpiPartial, s);
+  if (e != hipSuccess) return hip_fail(e, "int4_linear: gemm");
+  e = launch_reduce(ws.part, p.splits, batch, ps.n, nullptr, nullptr, out,
+                    proj == FUTX_PROJ_GATEUP ? dims->intermediate : 0, s);
+  if (e != hipSuccess) return hip_fail(e, "int4_linear: reduce");
   return FUTX_OK;
 }
 

@@ -75,11 +75,16 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16 bits, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// two fp32 -> packed bf16 pair (a in the low half), round to nearest even
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {

@@ -1,0 +1,62 @@
+// INT4 projection GEMM (gemm.hip): arguments, epilogues, planning.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace futx {
+
+// LDS budget of a workgroup's staged activation range (two workgroups per
+// CU fit), and the largest LDS allocation of one workgroup (gfx950: 160 KB).
+constexpr long kLdsActBudget = 72 * 1024;
+constexpr long kLdsMax = 160 * 1024;
+
+// Epilogues of int4_gemm_kernel.
+constexpr int kEpiPartial = 0;  // out[split][b][n] = partial sum (fp32, physical rows)
+constexpr int kEpiRms = 1;      // out[b][n] = sum / r_b, r_b = RMS of the fp32 activation row
+constexpr int kEpiResid = 2;    // out[b][n] = resid[b][n] + sum
+constexpr int kEpiSwiglu = 3;   // out_bf16[b][c] = bf16(silu(g / r_b) * u / r_b) for gate/up tile pairs
+
+struct GemmArgs {
+  const uint4* w;        // packed weights (layout.h)
+  const uint16_t* sc;    // fp16 group scales [N][K / G]
+  const void* act;       // activations: bf16 [terms][B][K] or fp32 [B][K]
+  size_t term_stride;    // elements between bf16 terms
+  int N, K, B;
+  int splits;            // K splits
+  int kb_per_wg;         // K blocks (128 inputs) per split
+  int items;             // 16-row tiles (gate/up pairs for kEpiSwiglu)
+  int wgs_per_split;     // workgroups per split, each with a run of items
+  float eps;             // RMSNorm epsilon
+  const float* resid;    // kEpiResid
+  float* out;            // kEpiPartial / kEpiRms / kEpiResid
+  uint16_t* out_bf16;    // kEpiSwiglu
+  int inter;             // kEpiSwiglu: row stride (intermediate size) of out_bf16
+};
+
+struct GemmPlan2 {
+  int splits = 1;
+  int kb_per_wg = 1;
+  int items = 1;
+  int wgs_per_split = 1;
+};
+
+// Work plan: K splits (only kEpiPartial splits K, until the activation
+// range fits the LDS budget) and workgroups per split.
+GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi);
+// Whether the single-split plan of an epilogue fits in LDS (otherwise the
+// caller splits K with kEpiPartial and finishes with separate kernels).
+bool gemm_fits(int K, int G, int B, int nterms, int epi);
+int device_cu_count();
+void apply_plan(GemmArgs& a, const GemmPlan2& p);
+hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi, hipStream_t st);
+
+inline void apply_plan(GemmArgs& a, const GemmPlan2& p) {
+  a.splits = p.splits;
+  a.kb_per_wg = p.kb_per_wg;
+  a.items = p.items;
+  a.wgs_per_split = p.wgs_per_split;
+}
+
+}  // namespace futx

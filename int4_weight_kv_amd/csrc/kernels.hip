@@ -617,6 +617,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(
     out_bf16[at] = t0;
     out_bf16[at + term_stride] = t1;
     out_bf16[at + 2 * term_stride] = t2;
+    if (!gsum) return;
     // group sums (groups of G = 64 or 128 channels inside the head)
     const double s = wave_sum_f64((double)bf16_bits_to_f32(t0) + (double)bf16_bits_to_f32(t1) +
                                   (double)bf16_bits_to_f32(t2));
