@@ -62,7 +62,7 @@ typedef int32_t futx_status;
 /* Shape of one decoder block.  Supported: head_dim in {64, 128}; w_group in
  * {64, 128}; had_block in {32, 64} dividing head_dim; page_size 64;
  * hidden, n_heads*head_dim and intermediate multiples of 128 and of
- * w_group; head_dim a multiple of w_group; n_heads a multiple of n_kv_heads
+ * 2*w_group (an even number of scale groups per weight row); head_dim a multiple of w_group; n_heads a multiple of n_kv_heads
  * with n_heads / n_kv_heads <= 16. */
 typedef struct futx_dims {
   int32_t hidden;

@@ -59,7 +59,8 @@ futx_status check_dims(const futx_dims* d) {
   if (d->head_dim % d->w_group) return fail(FUTX_E_UNSUPPORTED, "head_dim must be a multiple of w_group");
   const int ks[3] = {d->hidden, d->n_heads * d->head_dim, d->intermediate};
   for (int k : ks)
-    if (k % kTileK || k % d->w_group) return fail(FUTX_E_UNSUPPORTED, "projection inputs must be multiples of 128");
+    if (k % kTileK || k % (2 * d->w_group))
+      return fail(FUTX_E_UNSUPPORTED, "projection inputs must be multiples of 128 and of 2 * w_group");
   if (d->hidden % kTileN || d->intermediate % kTileN) return fail(FUTX_E_UNSUPPORTED, "bad row count");
 
   return FUTX_OK;
@@ -167,7 +168,7 @@ futx_status futx_packed_sizes(const futx_dims* dims, futx_proj proj, size_t* pac
   if (!packed_bytes || !scale_bytes) return fail(FUTX_E_ARG, "null output pointer");
   ProjShape s = proj_shape(*dims, proj);
   *packed_bytes = (size_t)s.n * s.k / 2;
-  *scale_bytes = (size_t)s.n * (s.k / dims->w_group) * 2;
+  *scale_bytes = 2 * scale_count(s.n, s.k / kTileK, dims->w_group);
   return FUTX_OK;
 }
 
@@ -304,7 +305,7 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
     a.out = out;
     a.out_bf16 = out_bf16;
     a.inter = I;
-    if (gemm_fits(K, G, B, nterms, epi)) {
+    if (gemm_fits(N, K, G, B, nterms, epi)) {
       apply_plan(a, plan_gemm(N, K, G, B, nterms, epi));
       return launch_int4_gemm(a, G, nterms, f32, epi, s);
     }

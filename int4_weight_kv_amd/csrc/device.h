@@ -42,6 +42,31 @@ __device__ __forceinline__ bf16x8 widen_word(uint32_t w) {
 // packed fp16 subtraction of 136 per pair leaves code = n - 8, which is
 // exactly representable.  Used where the operand offset must not enter the
 // fp32 accumulation (attention).
+// widen_word with three shifts and four 3-operand and-or ops (7 VALU ops per
+// word).  gfx9 VOP3 encodings take no literal operand, so with the mask and
+// magic as literals the compiler emits a separate and + or; the caller
+// passes them as opaque registers (mask scalar, magic vector: one scalar
+// operand per instruction), made with nib_regs().  No instruction is written
+// in inline asm: the compiler must see every VALU write that feeds a matrix
+// core instruction to insert its wait states.
+struct NibRegs {
+  uint32_t mask, magic;
+};
+__device__ __forceinline__ NibRegs nib_regs() {
+  NibRegs r{kNibMask, kMagic};
+  asm volatile("" : "+s"(r.mask));  // no instruction: hides the constant
+  asm volatile("" : "+v"(r.magic));
+  return r;
+}
+__device__ __forceinline__ bf16x8 widen_word_fast(uint32_t w, NibRegs k) {
+  u32x4 r;
+  r.x = (w & k.mask) | k.magic;
+  r.y = ((w >> 4) & k.mask) | k.magic;
+  r.z = ((w >> 8) & k.mask) | k.magic;
+  r.w = (__builtin_amdgcn_alignbit(w, w, 12) & k.mask) | k.magic;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 __device__ __forceinline__ f16x8 widen_word_exact_f16(uint32_t w) {
   u32x4 r;
   r.x = (w & kNibMask) | 0x58005800u;

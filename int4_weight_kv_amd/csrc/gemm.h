@@ -35,6 +35,26 @@ struct GemmArgs {
   int inter;             // kEpiSwiglu: row stride (intermediate size) of out_bf16
 };
 
+// LDS carve of int4_gemm_kernel (byte offsets, each 16-byte aligned).
+struct GemmLds {
+  size_t act, gsum, sqg, part, ss, out, scl, total;
+};
+__host__ __device__ inline GemmLds gemm_lds_layout(int nterms, int B, int krange, int G, int ntw, int nfr,
+                                                   int items_wg, int nkb8) {
+  auto up = [](size_t x) { return (x + 15) & ~(size_t)15; };
+  const int ngr = krange * 128 / G;
+  GemmLds l;
+  l.act = 0;
+  l.gsum = up(l.act + (size_t)nterms * B * (krange * 128 + 8) * 2);
+  l.sqg = up(l.gsum + (size_t)B * ngr * 8);
+  l.part = up(l.sqg + (size_t)B * ngr * 4);
+  l.ss = up(l.part + (size_t)2 * 4 * ntw * nfr * 64 * 4);
+  l.out = up(l.ss + (size_t)B * 4);
+  l.scl = up(l.out + (size_t)items_wg * ntw * B * 16 * 4);
+  l.total = up(l.scl + (size_t)items_wg * ntw * nkb8 * 16 * (8 * 128 / G) * 2);
+  return l;
+}
+
 struct GemmPlan2 {
   int splits = 1;
   int kb_per_wg = 1;
@@ -47,7 +67,7 @@ struct GemmPlan2 {
 GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi);
 // Whether the single-split plan of an epilogue fits in LDS (otherwise the
 // caller splits K with kEpiPartial and finishes with separate kernels).
-bool gemm_fits(int K, int G, int B, int nterms, int epi);
+bool gemm_fits(int N, int K, int G, int B, int nterms, int epi);
 int device_cu_count();
 void apply_plan(GemmArgs& a, const GemmPlan2& p);
 hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi, hipStream_t st);

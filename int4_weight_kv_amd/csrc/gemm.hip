@@ -10,30 +10,46 @@
 // the way").
 //
 // Work decomposition.  A workgroup owns a run of items (16-row weight
-// tiles; for the SwiGLU projection gate/up tile pairs) over one K range.  It
-// first stages that K range of the activation (all batch rows) in LDS as
-// bf16 matrix-core operands (an fp32 source is rounded to bf16 there, which
-// is the RMSNorm operand rounding), together with the exact (fp64) sum of
-// those operands per weight group, which removes the nibble offset, and for
-// an fp32 source the RMSNorm sum of squares.  Then each of its four waves
-// streams its quarter of the K range of item after item: 128-bit loads, 16
-// bytes per lane per 1 KB tile, in chunks of eight tiles with the next
-// chunk always in flight, across item boundaries.  At the end of an item the
-// four quarter sums are added in LDS and one wave (rotating) applies the
-// epilogue while the others keep streaming.
+// tiles; for the SwiGLU projection gate/up tile pairs) over one K range, and
+// each of its four waves owns a quarter of that K range for every item.  A
+// wave first stages its own quarter of the activation (all batch rows) in
+// LDS as bf16 matrix-core operands (an fp32 source is rounded to bf16 there,
+// which is the RMSNorm operand rounding), together with the exact (fp64) sum
+// of those operands per weight group, which removes the nibble offset, and
+// for an fp32 source the partial RMSNorm sum of squares; no barrier is
+// needed, since a wave reads only what it wrote.  The activation loads go
+// out before the weight loads and are converted while the weights stream.
+// Then the wave streams its quarter of item after item: 128-bit loads, 16
+// bytes per lane per 1 KB tile, in chunks of eight tiles (four for gate/up
+// pairs or batches above 16) with the next chunk in flight across item
+// boundaries.  At the end of an item the four quarter sums are added in LDS
+// and one wave (rotating) keeps them; the epilogue and the only global
+// stores run after the last item.
+//
+// Every vector load of the main loop is unconditional: loads complete in
+// order, so the compiler's wait before a use then covers exactly the loads
+// issued before it, and the chunk after the one in use stays in flight.
+#include <type_traits>
+
 #include "device.h"
 #include "gemm.h"
 
 namespace futx {
 
-template <int G, int NF, int NT, bool F32, int EPI, int PAIR>
-__global__ __launch_bounds__(256) void int4_gemm_kernel(GemmArgs a) {
-  constexpr int NTW = PAIR ? 2 : 1;   // weight tiles per item (gate + up)
-  constexpr int CHK = PAIR ? 4 : 8;   // K blocks per chunk and wave
+// Register budget: three waves per SIMD for G = 128 and a batch of up to 16,
+// otherwise two or one.
+template <int G, int NF, int NR, int NT, bool F32, int EPI, int PAIR>
+__global__ __launch_bounds__(256, (NF == 1 && G == 128) ? 2 : 1) void int4_gemm_kernel(GemmArgs a) {
+  constexpr int NTW = PAIR ? 2 : 1;                  // weight tiles per item (gate + up)
+  constexpr int CHK = (PAIR || NF == 2) ? 4 : 8;     // K blocks per chunk and wave
+  constexpr int MAXP = 4;                            // activation passes held in registers
   extern __shared__ __align__(16) uint8_t s_dyn[];
-  // LDS: activation range [NT][B][row] bf16 | group sums [B][ngr] float2 |
-  //      partials [2][4][NTW][NF][4][64] float | ss [B] float
-  const int tid = threadIdx.x, lane = tid & 63, wq = tid >> 6;
+  // LDS (gemm_lds_layout): activation range [NT][B][row] bf16 | group sums
+  // [B][ngr] float2 | group sums of squares [B][ngr] | partials
+  // [2][4][NTW][NF][NR][64] | ss [B] | item sums [item - it0][NTW][B][16] |
+  // scales
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int col = lane & 15, grp = lane >> 4;
   const int B = a.B;
   const int KB = a.K >> 7;
@@ -44,24 +60,32 @@ __global__ __launch_bounds__(256) void int4_gemm_kernel(GemmArgs a) {
   const int it1 = (int)((long)(wj + 1) * a.items / a.wgs_per_split);
   const int row = krange * 128 + 8;  // bf16 elements per LDS row (16 B pad)
   const int ngr = krange * 128 / G;
-  uint16_t* const s_act = (uint16_t*)s_dyn;
-  float2* const s_gsum = (float2*)(s_dyn + (size_t)NT * B * row * 2);
-  float* const s_part = (float*)(s_gsum + (size_t)B * ngr);
-  float* const s_ss = s_part + 2 * 4 * NTW * NF * 4 * 64;
-  const int ngroups = a.K / G;
+  constexpr int SEG = 8 * (128 / G);  // scales per (row, 8 K blocks)
+  const int KB8 = (KB + 7) >> 3;
+  const int b80 = kb0 >> 3, nkb8 = ((kb1 + 7) >> 3) - b80;
+  const GemmLds L = gemm_lds_layout(NT, B, krange, G, NTW, NF * NR, it1 - it0, nkb8);
+  uint16_t* const s_act = (uint16_t*)(s_dyn + L.act);
+  float2* const s_gsum = (float2*)(s_dyn + L.gsum);
+  float* const s_sqg = (float*)(s_dyn + L.sqg);
+  float* const s_part = (float*)(s_dyn + L.part);
+  float* const s_ss = (float*)(s_dyn + L.ss);
+  float* const s_out = (float*)(s_dyn + L.out);
+  // scales of the workgroup's items over its K range, blocked as in global
+  // memory: [item - it0][NTW][kb / 8 - kb0 / 8][row 16][SEG]
+  uint16_t* const s_scl = (uint16_t*)(s_dyn + L.scl);
 
   // this wave's quarter of the K range, in chunks of CHK K blocks
   const int kbq = (krange + 3) / 4;
   const int q0 = min(kb0 + wq * kbq, kb1), q1 = min(q0 + kbq, kb1);
   const int cpi = (kbq + CHK - 1) / CHK;  // chunks per item (same for every wave)
   const int nchunks = (it1 - it0) * cpi;
+  if (nchunks == 0) return;  // the whole workgroup: before any barrier
 
+  // ---- weights: the main loop issues weight loads only (scales come from LDS)
   uint4 wA[CHK][NTW], wB[CHK][NTW];
-  uint32_t sA[CHK][NTW][128 / G], sB[CHK][NTW][128 / G];
-  // Loads are unconditional (out-of-range K blocks re-read the quarter's
-  // first block and are not used) and scales stay raw bits until use, so
-  // a wave never waits on one chunk while loading the next.
-  auto load_chunk = [&](uint4 (&w)[CHK][NTW], uint32_t (&sc)[CHK][NTW][128 / G], int c) {
+  // Out-of-range K blocks of a chunk re-read the quarter's first block and
+  // are weighted by zero.
+  auto load_chunk = [&](uint4 (&w)[CHK][NTW], int c) {
     const int item = it0 + c / cpi, cb = q0 + (c % cpi) * CHK;
 #pragma unroll
     for (int i = 0; i < CHK; ++i) {
@@ -69,71 +93,95 @@ __global__ __launch_bounds__(256) void int4_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int u = 0; u < NTW; ++u) {
         const int nt = PAIR ? 2 * item + u : item;
-        w[i][u] = a.w[((size_t)nt * KB + kb) * 64 + lane];
-#pragma unroll
-        for (int gi = 0; gi < 128 / G; ++gi)
-          sc[i][u][gi] = a.sc[(size_t)(nt * 16 + col) * ngroups + kb * (128 / G) + gi];
+        const uint4* wt = a.w + ((size_t)nt * KB + kb) * 64;
+        w[i][u] = wt[lane];
       }
     }
   };
-  if (nchunks > 0) load_chunk(wA, sA, 0);
-  if (nchunks > 1) load_chunk(wB, sB, 1);
 
-  // ---- stage the activation range once: bf16 operands, exact group sums,
-  // RMSNorm sum of squares (deterministic order)
-  {
-    const int c8 = krange * 16;  // 8-element chunks per row
-    const int total = B * c8;
-    for (int it = 0; it * 256 < total; ++it) {
-      const int idx = it * 256 + tid;
-      const bool ok = idx < total;
-      const int b = ok ? idx / c8 : 0, k8 = ok ? idx - b * c8 : 0;
-      double gs = 0.0;
-      float sq = 0.f;
-      if (ok) {
-        const size_t src = (size_t)b * a.K + kb0 * 128 + k8 * 8;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          uint4 v;
-          if constexpr (F32) {
-            const float4* q = (const float4*)((const float*)a.act + src);
-            const float4 x0 = q[0], x1 = q[1];
-            v = uint4{pack2_bf16(x0.x, x0.y), pack2_bf16(x0.z, x0.w), pack2_bf16(x1.x, x1.y), pack2_bf16(x1.z, x1.w)};
-            sq = fmaf(x0.x, x0.x, fmaf(x0.y, x0.y, fmaf(x0.z, x0.z, fmaf(x0.w, x0.w, sq))));
-            sq = fmaf(x1.x, x1.x, fmaf(x1.y, x1.y, fmaf(x1.z, x1.z, fmaf(x1.w, x1.w, sq))));
-          } else {
-            v = *(const uint4*)((const uint16_t*)a.act + t * a.term_stride + src);
-          }
-          *(uint4*)(s_act + (size_t)(t * B + b) * row + k8 * 8) = v;
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            gs += (double)bf16_bits_to_f32(w4[c] & 0xFFFF) + (double)bf16_bits_to_f32(w4[c] >> 16);
-        }
-      }
-      // a weight group is G / 8 consecutive chunks = consecutive lanes
-#pragma unroll
-      for (int o = 1; o < G / 8; o <<= 1) {
-        gs += __shfl_xor(gs, o, 64);
-        if constexpr (F32) sq += __shfl_xor(sq, o, 64);
-      }
-      if (ok && (k8 % (G / 8)) == 0) {
-        s_gsum[(size_t)b * ngr + k8 / (G / 8)] = split_f64(gs);
-        if constexpr (F32) s_part[(size_t)b * ngr + k8 / (G / 8)] = sq;  // scratch until the loop
-      }
-    }
-    __syncthreads();
+  // ---- scale staging: 16-byte pieces; piece p = ((il * NTW + u) * nkb8 +
+  // j) * 16 * (SEG / 8) + r covers row r / (SEG / 8), part r % (SEG / 8)
+  constexpr int MAXS = 4;  // pieces per thread held in registers
+  const int npieces = (it1 - it0) * NTW * nkb8 * 16 * (SEG / 8);
+  auto scl_src = [&](int p) -> const uint4* {
+    const int per_blk = 16 * (SEG / 8);
+    const int blk = p / per_blk, r = p - blk * per_blk;
+    const int j = blk % nkb8, iu = blk / nkb8;
+    const int nt = PAIR ? 2 * (it0 + iu / NTW) + iu % NTW : it0 + iu;
+    return (const uint4*)(a.sc + ((size_t)nt * KB8 + b80 + j) * 16 * SEG) + r;
+  };
+
+  // ---- activation staging of this wave's quarter: pass p covers row
+  // p / ppr, elements [(p % ppr) * 512, +512) of the quarter, 8 per lane
+  const int qk = (q1 - q0) * 128;
+  const int ppr = (qk + 511) >> 9;
+  const int npass = B * ppr;
+  using ActRegs = typename std::conditional<F32, float4[2], uint4[NT]>::type;
+  auto act_load = [&](int p, ActRegs& r) {  // p < 0 (empty quarter): row 0, a valid address
+    p = p < 0 ? 0 : p;
+    const int b = ppr ? p / ppr : 0, e = (p - b * ppr) * 512 + lane * 8;
+    const size_t src = (size_t)b * a.K + q0 * 128 + (e < qk ? e : 0);
     if constexpr (F32) {
-      if (tid < B) {
-        float t = 0.f;
-        for (int g = 0; g < ngr; ++g) t += s_part[(size_t)tid * ngr + g];
-        s_ss[tid] = t;
-      }
-      __syncthreads();
+      const float4* q = (const float4*)((const float*)a.act + src);
+      r[0] = q[0];
+      r[1] = q[1];
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) r[t] = *(const uint4*)((const uint16_t*)a.act + t * a.term_stride + src);
     }
-  }
+  };
+  auto act_store = [&](int p, const ActRegs& r) {
+    const int b = p / ppr, e = (p - b * ppr) * 512 + lane * 8;
+    const bool ok = e < qk;
+    const int kl = (q0 - kb0) * 128 + e;  // offset in the workgroup's K range
+    double gs = 0.0;
+    float sq = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint4 v;
+      if constexpr (F32) {
+        const float4 x0 = r[0], x1 = r[1];
+        v = uint4{pack2_bf16(x0.x, x0.y), pack2_bf16(x0.z, x0.w), pack2_bf16(x1.x, x1.y), pack2_bf16(x1.z, x1.w)};
+        sq = fmaf(x0.x, x0.x, fmaf(x0.y, x0.y, fmaf(x0.z, x0.z, fmaf(x0.w, x0.w, sq))));
+        sq = fmaf(x1.x, x1.x, fmaf(x1.y, x1.y, fmaf(x1.z, x1.z, fmaf(x1.w, x1.w, sq))));
+      } else {
+        v = r[t];
+      }
+      if (ok) *(uint4*)(s_act + (size_t)(t * B + b) * row + kl) = v;
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        gs += (double)bf16_bits_to_f32(w4[c] & 0xFFFF) + (double)bf16_bits_to_f32(w4[c] >> 16);
+    }
+    // a weight group is G / 8 consecutive lanes
+#pragma unroll
+    for (int o = 1; o < G / 8; o <<= 1) {
+      gs += __shfl_xor(gs, o, 64);
+      if constexpr (F32) sq += __shfl_xor(sq, o, 64);
+    }
+    if (ok && (lane % (G / 8)) == 0) {
+      s_gsum[(size_t)b * ngr + kl / G] = split_f64(gs);
+      if constexpr (F32) s_sqg[(size_t)b * ngr + kl / G] = sq;
+    }
+  };
 
-  // ---- stream: chunk c of item it0 + c / cpi
+  // Batch placement in the matrix-core tile: A row `col` of fragment f holds
+  // batch 16f + 4(col % 4) + col / 4, so D register r of lane group grp holds
+  // batch 16f + 4r + grp and a batch of at most 4 needs D register 0 only.
+  // A rows past the batch repeat a valid row; their results are never used.
+  uint32_t a_off[NT][NF];  // LDS byte offset of this lane's A row at k = grp * 8
+  int b_of[NF][NR];        // batch held by D register r (>= B: unused)
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    int bb = 16 * f + 4 * (col & 3) + (col >> 2);
+    if (bb >= B) bb = 16 * f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) a_off[t][f] = (uint32_t)(((t * B + bb) * row + grp * 8) * 2);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) b_of[f][r] = 16 * f + 4 * r + grp;
+  }
+  const NibRegs nib = nib_regs();
+
   f32x4 acc[NTW][NF];
   auto zero_acc = [&]() {
 #pragma unroll
@@ -141,50 +189,57 @@ __global__ __launch_bounds__(256) void int4_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[u][f] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  zero_acc();
 
-  auto compute = [&](const uint4 (&w)[CHK][NTW], const uint32_t (&sc)[CHK][NTW][128 / G], int c) {
+  const uint32_t scl_lane = (uint32_t)col * SEG;
+  auto compute = [&](const uint4 (&w)[CHK][NTW], int c) {
+    if (q0 >= q1) return;  // empty quarter (uniform): nothing staged to read
     const int cb = q0 + (c % cpi) * CHK;
+    const int il = c / cpi;
+    const uint8_t* const s_act_c = (const uint8_t*)s_act;
+    // branch-free: a K block past the quarter was loaded from a valid block
+    // and is weighted by zero
 #pragma unroll
     for (int i = 0; i < CHK; ++i) {
-      const int kb = cb + i;
-      if (kb < q1) {
-        const int kl = (kb - kb0) * 128;
+      const bool live = cb + i < q1;
+      const int kb = live ? cb + i : (q0 < q1 ? q0 : kb0);
 #pragma unroll
-        for (int gi = 0; gi < 128 / G; ++gi) {
-          f32x4 d[NTW][NF];
+      for (int gi = 0; gi < 128 / G; ++gi) {
+        f32x4 d[NTW][NF];
 #pragma unroll
-          for (int u = 0; u < NTW; ++u)
+        for (int u = 0; u < NTW; ++u)
 #pragma unroll
-            for (int f = 0; f < NF; ++f) d[u][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int f = 0; f < NF; ++f) d[u][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ss = 0; ss < G / 32; ++ss) {
-            const int s = gi * (G / 32) + ss;
-            bf16x8 bw[NTW];
+        for (int ss = 0; ss < G / 32; ++ss) {
+          const int s = gi * (G / 32) + ss;
+          bf16x8 bw[NTW];
 #pragma unroll
-            for (int u = 0; u < NTW; ++u) bw[u] = widen_word(word_of(w[i][u], s));
+          for (int u = 0; u < NTW; ++u) bw[u] = widen_word_fast(word_of(w[i][u], s), nib);
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+          for (int t = 0; t < NT; ++t)
 #pragma unroll
-              for (int f = 0; f < NF; ++f) {
-                const int tok = f * 16 + col;
-                uint4 v = {0u, 0u, 0u, 0u};
-                if (tok < B) v = *(const uint4*)(s_act + (size_t)(t * B + tok) * row + kl + s * 32 + grp * 8);
-                const bf16x8 av = as_bf16x8(v);
+            for (int f = 0; f < NF; ++f) {
+              const bf16x8 av = *(const bf16x8*)(s_act_c + a_off[t][f] + (kb - kb0) * 256 + s * 64);
 #pragma unroll
-                for (int u = 0; u < NTW; ++u) d[u][f] = mfma16(av, bw[u], d[u][f]);
-              }
-          }
-          const int jl = kl / G + gi;
+              for (int u = 0; u < NTW; ++u) d[u][f] = mfma16(av, bw[u], d[u][f]);
+            }
+        }
+        const int jl = (kb - kb0) * (128 / G) + gi;
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+          const uint16_t* st = s_scl + ((size_t)((il * NTW + u) * nkb8 + (kb >> 3) - b80) * 16) * SEG +
+                               (kb & 7) * (128 / G) + gi;
+          // read unconditionally (kb is clamped into the staged range), then
+          // select: no branch around the LDS read
+          const float sv = half_bits_to_f32(st[scl_lane]);
+          const float scale = live ? sv : 0.f;
 #pragma unroll
           for (int f = 0; f < NF; ++f)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int tok = f * 16 + 4 * grp + r;
-              const float2 gs = tok < B ? s_gsum[(size_t)tok * ngr + jl] : float2{0.f, 0.f};
-#pragma unroll
-              for (int u = 0; u < NTW; ++u)
-                acc[u][f][r] = fmaf(half_bits_to_f32((uint16_t)sc[i][u][gi]), remove_offset(d[u][f][r], gs), acc[u][f][r]);
+            for (int r = 0; r < NR; ++r) {
+              const int b = b_of[f][r] < B ? b_of[f][r] : 0;
+              const float2 gs = s_gsum[(size_t)b * ngr + jl];
+              acc[u][f][r] = fmaf(scale, remove_offset(d[u][f][r], gs), acc[u][f][r]);
             }
         }
       }
@@ -192,58 +247,128 @@ __global__ __launch_bounds__(256) void int4_gemm_kernel(GemmArgs a) {
   };
 
   auto part = [&](int slot, int w, int u, int f, int r) -> float& {
-    return s_part[((((slot * 4 + w) * NTW + u) * NF + f) * 4 + r) * 64 + lane];
+    return s_part[((((slot * 4 + w) * NTW + u) * NF + f) * NR + r) * 64 + lane];
   };
 
-  // end of an item: add the four quarters in LDS; one wave (rotating)
-  // applies the epilogue while the others go on streaming
+  // end of an item: add the four quarters in LDS; one wave (rotating) keeps
+  // the item's sums in LDS while the others go on streaming.  No global
+  // memory access happens here: on this target stores count in vmcnt too.
   auto finish_item = [&](int item, int slot) {
 #pragma unroll
     for (int u = 0; u < NTW; ++u)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part(slot, wq, u, f, r) = acc[u][f][r];
+        for (int r = 0; r < NR; ++r) part(slot, wq, u, f, r) = acc[u][f][r];
     zero_acc();
     __syncthreads();
     if (wq != ((item - it0) & 3)) return;
-    float o[NTW][NF][4];
 #pragma unroll
     for (int u = 0; u < NTW; ++u)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          o[u][f][r] = (part(slot, 0, u, f, r) + part(slot, 1, u, f, r)) + (part(slot, 2, u, f, r) + part(slot, 3, u, f, r));
-    const int n = item * 16 + col;  // physical row (non-pair) / logical column (pair)
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = f * 16 + 4 * grp + r;
-        if (tok >= B) continue;
-        if constexpr (EPI == kEpiPartial) {
-          a.out[((size_t)split * B + tok) * a.N + n] = o[0][f][r];
-        } else if constexpr (EPI == kEpiRms) {
-          a.out[(size_t)tok * a.N + n] = o[0][f][r] * (1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps));
-        } else if constexpr (EPI == kEpiResid) {
-          a.out[(size_t)tok * a.N + n] = a.resid[(size_t)tok * a.N + n] + o[0][f][r];
-        } else {  // kEpiSwiglu: u = 0 gate rows, u = 1 up rows of logical column n
-          const float invr = 1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps);
-          const float g = o[0][f][r] * invr, up = o[PAIR][f][r] * invr;
-          a.out_bf16[(size_t)tok * a.inter + n] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * up);
+        for (int r = 0; r < NR; ++r) {
+          const float o = (part(slot, 0, u, f, r) + part(slot, 1, u, f, r)) + (part(slot, 2, u, f, r) + part(slot, 3, u, f, r));
+          const int tok = b_of[f][r];
+          if (tok < B) s_out[(((item - it0) * NTW + u) * B + tok) * 16 + col] = o;
         }
-      }
+  };
+  auto finish = [&](int c) {
+    if ((c + 1) % cpi == 0) finish_item(it0 + c / cpi, (c / cpi) & 1);
   };
 
-  for (int c = 0; c < nchunks; c += 2) {
-    compute(wA, sA, c);
-    if (c + 2 < nchunks) load_chunk(wA, sA, c + 2);
-    if ((c + 1) % cpi == 0) finish_item(it0 + c / cpi, (c / cpi) & 1);
-    if (c + 1 < nchunks) {
-      compute(wB, sB, c + 1);
-      if (c + 3 < nchunks) load_chunk(wB, sB, c + 3);
-      if ((c + 2) % cpi == 0) finish_item(it0 + (c + 1) / cpi, ((c + 1) / cpi) & 1);
+  // Prologue: the activation loads (when they fit in registers) go out
+  // first, then the first weight chunk(s); staging then waits for the
+  // activation only.  Both staging paths end with only weight loads in
+  // flight.
+  auto prologue = [&](auto two_chunks) {
+    // scales first (oldest loads: waiting for them does not wait for
+    // weights); unconditional loads with clamped indices, since
+    // conditionally assigned register arrays are placed in scratch
+    uint4 sr[MAXS];
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k) sr[k] = *scl_src(min(k * 256 + tid, npieces - 1));
+    if (npass <= MAXP) {
+      ActRegs r[MAXP];
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p) act_load(min(p, npass - 1), r[p]);  // clamped; see above
+      load_chunk(wA, 0);
+      if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p)
+        if (p < npass) act_store(p, r[p]);
+    } else {
+      for (int p = 0; p < npass; ++p) {
+        ActRegs r;
+        act_load(p, r);
+        act_store(p, r);
+      }
+      load_chunk(wA, 0);
+      if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k)
+      if (k * 256 + tid < npieces) ((uint4*)s_scl)[k * 256 + tid] = sr[k];
+    // pieces beyond the registers (the planner avoids this; correct but slow)
+    for (int q = MAXS * 256 + tid; q < npieces; q += 256) ((uint4*)s_scl)[q] = *scl_src(q);
+    zero_acc();
+    __syncthreads();  // scales of the whole workgroup
+  };
+
+  if (nchunks == 1) {
+    prologue(std::false_type{});
+    compute(wA, 0);
+    finish(0);
+  } else {
+    prologue(std::true_type{});
+    // Main loop over chunk pairs with unconditional loads; the last one to
+    // three chunks are peeled.
+    int c = 0;
+    for (; c + 3 < nchunks; c += 2) {
+      compute(wA, c);
+      load_chunk(wA, c + 2);
+      finish(c);
+      compute(wB, c + 1);
+      load_chunk(wB, c + 3);
+      finish(c + 1);
+    }
+    compute(wA, c);
+    if (c + 2 < nchunks) load_chunk(wA, c + 2);
+    finish(c);
+    compute(wB, c + 1);
+    finish(c + 1);
+    if (c + 2 < nchunks) {
+      compute(wA, c + 2);
+      finish(c + 2);
+    }
+  }
+  __syncthreads();
+
+  // ---- epilogue and write-out of the workgroup's items
+  if constexpr (F32) {
+    if (tid < B) {  // RMSNorm sum of squares, fixed order
+      float t = 0.f;
+      for (int g = 0; g < ngr; ++g) t += s_sqg[(size_t)tid * ngr + g];
+      s_ss[tid] = t;
+    }
+    __syncthreads();
+  }
+  const int nout = (it1 - it0) * B * 16;
+  for (int idx = tid; idx < nout; idx += 256) {
+    const int il = idx / (B * 16), rem = idx - il * B * 16, tok = rem >> 4, cc = rem & 15;
+    const int n = (it0 + il) * 16 + cc;  // physical row (non-pair) / logical column (pair)
+    const float o = s_out[((il * NTW) * B + tok) * 16 + cc];
+    if constexpr (EPI == kEpiPartial) {
+      a.out[((size_t)split * B + tok) * a.N + n] = o;
+    } else if constexpr (EPI == kEpiRms) {
+      a.out[(size_t)tok * a.N + n] = o * (1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps));
+    } else if constexpr (EPI == kEpiResid) {
+      a.out[(size_t)tok * a.N + n] = a.resid[(size_t)tok * a.N + n] + o;
+    } else {  // kEpiSwiglu: u = 0 gate rows, u = 1 up rows of logical column n
+      const float invr = 1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps);
+      const float g = o * invr, up = s_out[((il * NTW + PAIR) * B + tok) * 16 + cc] * invr;
+      a.out_bf16[(size_t)tok * a.inter + n] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * up);
     }
   }
 }
@@ -263,17 +388,26 @@ int device_cu_count() {
 size_t gemm_lds_bytes(const GemmArgs& a, int nterms, int G, bool pair) {
   const int krange = a.kb_per_wg;
   const int nf = a.B <= 16 ? 1 : 2;
-  const size_t act = (size_t)nterms * a.B * ((size_t)krange * 128 + 8) * 2;
-  const size_t gs = (size_t)a.B * (krange * 128 / G) * 8;
-  const size_t prt = (size_t)2 * 4 * (pair ? 2 : 1) * nf * 4 * 64 * 4;
-  const size_t sq = (size_t)a.B * (krange * 128 / G) * 4;  // scratch, aliases the partials
-  return act + gs + (prt > sq ? prt : sq) + (size_t)a.B * 4;
+  const int nr = a.B <= 4 ? 1 : a.B <= 8 ? 2 : 4;
+  const int items_wg = (a.items + a.wgs_per_split - 1) / a.wgs_per_split;
+  const int nkb8 = (krange + 7) / 8 + 1;  // a K range not aligned to 8 blocks spans one more
+  return gemm_lds_layout(nterms, a.B, krange, G, pair ? 2 : 1, nf * nr, items_wg, nkb8).total;
+}
+
+static size_t plan_lds(const GemmPlan2& p, int B, int G, int nterms, bool pair) {
+  GemmArgs a{};
+  a.B = B;
+  a.kb_per_wg = p.kb_per_wg;
+  a.items = p.items;
+  a.wgs_per_split = p.wgs_per_split;
+  return gemm_lds_bytes(a, nterms, G, pair);
 }
 
 GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   GemmPlan2 p;
   const int KB = K / 128;
-  const int items = epi == kEpiSwiglu ? N / 32 : N / 16;
+  const bool pair = epi == kEpiSwiglu;
+  const int items = pair ? N / 32 : N / 16;
   // K splits: only kEpiPartial may split; split until the activation range
   // fits the LDS budget
   p.splits = 1;
@@ -282,20 +416,28 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   }
   p.kb_per_wg = (KB + p.splits - 1) / p.splits;
   p.splits = (KB + p.kb_per_wg - 1) / p.kb_per_wg;
-  // workgroups per split: about two per CU in total
-  const int cus = device_cu_count();
-  int w = (2 * cus + p.splits - 1) / p.splits;
-  p.wgs_per_split = w < items ? w : items;
   p.items = items;
+  // about three resident workgroups per CU in total (the register budget
+  // allows three 4-wave workgroups per CU); items are spread evenly, and a
+  // workgroup's item sums must fit LDS
+  const int cus = device_cu_count();
+  const int target = (3 * cus + p.splits - 1) / p.splits;
+  int per = (items + target - 1) / target;
+  if (per < 1) per = 1;
+  // scale staging: at most 1024 16-byte pieces per workgroup (registers)
+  const int nkb8 = (p.kb_per_wg + 7) / 8 + 1;
+  auto pieces = [&](int ipw) { return (long)ipw * (pair ? 2 : 1) * nkb8 * 16 * (128 / G); };
+  for (;;) {
+    p.wgs_per_split = (items + per - 1) / per;
+    if (per == 1 || (plan_lds(p, B, G, nterms, pair) <= (size_t)kLdsMax && pieces(per) <= 1024)) break;
+    --per;
+  }
   return p;
 }
 
-bool gemm_fits(int K, int G, int B, int nterms, int epi) {
-  GemmArgs a{};
-  a.B = B;
-  const GemmPlan2 p = plan_gemm(16, K, G, B, nterms, epi);
-  a.kb_per_wg = p.kb_per_wg;
-  return gemm_lds_bytes(a, nterms, G, epi == kEpiSwiglu) <= kLdsMax;
+bool gemm_fits(int N, int K, int G, int B, int nterms, int epi) {
+  const GemmPlan2 p = plan_gemm(N, K, G, B, nterms, epi);
+  return plan_lds(p, B, G, nterms, epi == kEpiSwiglu) <= (size_t)kLdsMax;
 }
 
 hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi, hipStream_t st) {
@@ -304,15 +446,18 @@ hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi
   if (a.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
   const size_t lds = gemm_lds_bytes(a, nterms, G, pair);
   if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
-#define FUTX_G(GG, NF, NT, F32, EPI, PR) \
+#define FUTX_G(GG, NF, NR, NT, F32, EPI, PR) \
   do {                                   \
-    auto k_ = int4_gemm_kernel<GG, NF, NT, F32, EPI, PR>; \
+    auto k_ = int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR>; \
     if (lds > 64 * 1024) hipFuncSetAttribute((const void*)k_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     k_<<<grid, block, lds, st>>>(a); \
   } while (0)
 #define FUTX_NF(GG, NT, F32, EPI, PR) \
   do {                                  \
-    if (a.B <= 16) FUTX_G(GG, 1, NT, F32, EPI, PR); else FUTX_G(GG, 2, NT, F32, EPI, PR); \
+    if (a.B <= 4) FUTX_G(GG, 1, 1, NT, F32, EPI, PR);                  \
+    else if (a.B <= 8) FUTX_G(GG, 1, 2, NT, F32, EPI, PR);             \
+    else if (a.B <= 16) FUTX_G(GG, 1, 4, NT, F32, EPI, PR);            \
+    else FUTX_G(GG, 2, 4, NT, F32, EPI, PR);                           \
   } while (0)
 #define FUTX_GRP(NT, F32, EPI, PR)                                        \
   do {                                                                     \

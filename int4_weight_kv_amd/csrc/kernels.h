@@ -22,26 +22,16 @@ struct KVPtrsConst {
   int nkv;
 };
 
-struct GemmPlan {
-  int kbps = 1;    // K blocks (128 inputs) per split
-  int splits = 1;  // K splits
-};
-
 struct AttnPlan {
   int chunk = 64;  // tokens per split (multiple of the page size)
   int nsplit = 1;  // splits per sequence for the largest context
 };
 
-GemmPlan gemm_plan(int N, int K);
 AttnPlan attn_plan(int B, int nkv, int max_context);
 
 hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* act, float* invr,
                            hipStream_t st);
 hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float2* gsum, hipStream_t st);
-// act: nterms (1 or 3) bf16 activation terms [B][K], term t at act + t * term_stride
-hipError_t launch_gemm_partial(const void* wpk, const void* wsc, const uint16_t* act, int nterms,
-                               size_t term_stride, const float2* gsum, int B, int N, int K, int G,
-                               float* part, const GemmPlan& plan, hipStream_t st);
 hipError_t launch_reduce(const float* part, int S, int B, int N, const float* rowscale,
                          const float* resid, float* out, int gateup_inter, hipStream_t st);
 hipError_t launch_swiglu(const float* part, int S, int B, int I, int G, const float* invr,

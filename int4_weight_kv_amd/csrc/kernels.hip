@@ -49,94 +49,18 @@ __global__ __launch_bounds__(64) void gsum_kernel(const uint16_t* __restrict__ a
   if (threadIdx.x == 0) gsum[j * kMaxBatch + b] = split_f64(s);
 }
 
-// ---------------------------------------------------------------- INT4 GEMM
+// ---------------------------------------------------- split-K epilogues
+// (the INT4 GEMM itself is in gemm.hip; with K split it writes fp32 partial
+// sums part[split][b][P] in physical row order, finished here)
 
-// Split-K partial products of one packed projection.  One wave per
-// (16-row tile, K split); per K block it loads 16 bytes of nibbles per lane
-// (four MFMA steps), widens them to bf16 in registers and multiplies with
-// the bf16 activations (NT = 3: an activation given as a sum of three bf16
-// terms, accumulated in the same fp32 sum).  Per weight group the MFMA sum is corrected for the
-// nibble offset with the exact activation group sum and scaled by the group
-// scale.
-// part[split][b][P] (fp32, physical row order).
-template <int G, int NF, int NT>
-__global__ __launch_bounds__(256) void gemm_partial_kernel(
-    const uint4* __restrict__ wpk, const uint16_t* __restrict__ wsc,
-    const uint16_t* __restrict__ act, size_t term_stride, const float2* __restrict__ gsum, int B,
-    int N, int K, int kbps, int S, float* __restrict__ part) {
-  const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int ntiles = N / 16;
-  if (wid >= ntiles * S) return;
-  const int nt = wid / S, split = wid - nt * S;
-  const int KB = K / 128;
-  const int kb0 = split * kbps, kb1 = min(kb0 + kbps, KB);
-  const int col = lane & 15, grp = lane >> 4;
-  const int n = nt * 16 + col;
-  const int ngroups = K / G;
-  f32x4 acc[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const uint4 wv = wpk[((size_t)nt * KB + kb) * 64 + lane];
-    bf16x8 a[NT][NF][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int tok = f * 16 + col;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint4 av = {0u, 0u, 0u, 0u};
-          if (tok < B)
-            av = *(const uint4*)(act + t * term_stride + (size_t)tok * K + kb * 128 + s * 32 + grp * 8);
-          a[t][f][s] = as_bf16x8(av);
-        }
-      }
-#pragma unroll
-    for (int gi = 0; gi < 128 / G; ++gi) {
-      f32x4 d[NF];
-#pragma unroll
-      for (int f = 0; f < NF; ++f) d[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ss = 0; ss < G / 32; ++ss) {
-        const int s = gi * (G / 32) + ss;
-        const bf16x8 bw = widen_word(word_of(wv, s));
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int f = 0; f < NF; ++f) d[f] = mfma16(a[t][f][s], bw, d[f]);
-      }
-      const int j = kb * (128 / G) + gi;
-      const float sc = half_bits_to_f32(wsc[(size_t)n * ngroups + j]);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = f * 16 + 4 * grp + r;
-          const float2 gs = tok < B ? gsum[j * kMaxBatch + tok] : float2{0.f, 0.f};
-          acc[f][r] = fmaf(sc, remove_offset(d[f][r], gs), acc[f][r]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = f * 16 + 4 * grp + r;
-      if (tok < B) part[((size_t)split * B + tok) * N + n] = acc[f][r];
-    }
-  }
-}
-
+// logical row n of a projection output -> physical row (GATEUP tiles
+// alternate gate / up; identity otherwise)
 __device__ __forceinline__ int physical_row(int n, int gateup_inter) {
   if (!gateup_inter) return n;
   const int half = n / gateup_inter, r = n - half * gateup_inter;
   return (2 * (r >> 4) + half) * 16 + (r & 15);
 }
 
-// out[b][n] = resid[b][n] + rowscale[b] * sum_s part[s][b][P(n)]  (n logical)
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int S, int B,
                                                      int N, const float* __restrict__ rowscale,
                                                      const float* resid, float* out,
@@ -652,45 +576,6 @@ hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* ac
 
 hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float2* gsum, hipStream_t st) {
   gsum_kernel<<<dim3(K / G, B), 64, 0, st>>>(act, K, G, gsum);
-  FUTX_LAUNCH_CHECK();
-  return hipSuccess;
-}
-
-GemmPlan gemm_plan(int N, int K) {
-  GemmPlan p;
-  const int kblocks = K / 128, ntiles = N / 16;
-  int s = (2048 + ntiles - 1) / ntiles;
-  s = s < 1 ? 1 : s;
-  s = s > 16 ? 16 : s;
-  s = s > kblocks ? kblocks : s;
-  p.kbps = (kblocks + s - 1) / s;
-  p.splits = (kblocks + p.kbps - 1) / p.kbps;
-  return p;
-}
-
-hipError_t launch_gemm_partial(const void* wpk, const void* wsc, const uint16_t* act, int nterms,
-                               size_t term_stride, const float2* gsum, int B, int N, int K, int G,
-                               float* part, const GemmPlan& plan, hipStream_t st) {
-  const int waves = (N / 16) * plan.splits;
-  const dim3 grid((waves + 3) / 4), block(256);
-  const uint4* w = (const uint4*)wpk;
-  const uint16_t* s = (const uint16_t*)wsc;
-#define FUTX_GEMM(GG, NF, NT) \
-  gemm_partial_kernel<GG, NF, NT><<<grid, block, 0, st>>>(w, s, act, term_stride, gsum, B, N, K, plan.kbps, plan.splits, part)
-  if (nterms == 3) {
-    if (G == 128) {
-      if (B <= 16) FUTX_GEMM(128, 1, 3); else FUTX_GEMM(128, 2, 3);
-    } else {
-      if (B <= 16) FUTX_GEMM(64, 1, 3); else FUTX_GEMM(64, 2, 3);
-    }
-  } else {
-    if (G == 128) {
-      if (B <= 16) FUTX_GEMM(128, 1, 1); else FUTX_GEMM(128, 2, 1);
-    } else {
-      if (B <= 16) FUTX_GEMM(64, 1, 1); else FUTX_GEMM(64, 2, 1);
-    }
-  }
-#undef FUTX_GEMM
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }

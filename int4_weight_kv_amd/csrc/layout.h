@@ -28,7 +28,8 @@
 //   packed[nt][kb][L][16 bytes], nt = row tile (16 rows), kb = K block (128),
 //   word s (bytes 4s..4s+3) of lane L holds row nt*16 + L%16 and inputs
 //   kb*128 + 32 s + 8 (L/16) + e.
-//   scales[P][K/G] fp16, P = physical row.
+//   scales fp16 [nt][kb / 8][i 16][8 * 128 / G]: row P = nt*16 + i, group g
+//   of K block kb = g * G / 128 at position (kb % 8) * 128 / G + g % (128 / G).
 // Physical rows equal logical rows except GATEUP, whose 16-row tiles
 // alternate gate / up: physical tile 2t holds gate rows 16t..16t+15 and
 // tile 2t+1 holds up rows 16t..16t+15, so one wave sees both halves of a
@@ -83,6 +84,20 @@ inline void weight_nibble_pos(int P, int k, int kblocks, size_t* word_off, int* 
   int lane = g * 16 + i;
   *word_off = weight_tile_offset(nt, kb, kblocks) + (size_t)lane * 16 + (size_t)s * 4;
   *elem = e;
+}
+
+// Group scales, fp16, blocked by weight tile: [nt][kb / 8][row i 16][groups
+// of those 8 K blocks], i.e. 8 * 128 / group scales per (tile row, 8 K
+// blocks), the last block padded when the K block count is not a multiple
+// of 8.  One tile's 16 scales share a 32-byte (group 128) run.
+inline int scale_kb_blocks(int kblocks) { return (kblocks + 7) / 8; }
+inline size_t scale_count(int n, int kblocks, int group) {
+  return (size_t)n * scale_kb_blocks(kblocks) * 8 * (kTileK / group);
+}
+inline size_t scale_index(int P, int g, int kblocks, int group) {
+  const int per_kb = kTileK / group, seg = 8 * per_kb;
+  const int nt = P / kTileN, i = P % kTileN, kb = g / per_kb, gi = g % per_kb;
+  return (((size_t)nt * scale_kb_blocks(kblocks) + kb / 8) * kTileN + i) * seg + (kb % 8) * per_kb + gi;
 }
 
 // GATEUP: physical row of logical row n (0..2I-1); identity for the others.

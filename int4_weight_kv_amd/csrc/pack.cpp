@@ -87,7 +87,7 @@ bool pack_rows(const PackJob& j, int r0, int r1) {
       for (int c = 0; c < j.group; ++c) a = std::fmax(a, std::fabs(x[c]));
       uint16_t s16 = f32_to_f16_rne(a / 7.0f);
       if ((s16 & 0x7C00u) == 0x7C00u) return false;
-      j.scales[(size_t)P * ngroups + g] = s16;
+      j.scales[scale_index(P, g, j.kblocks, j.group)] = s16;
       float sf = f16_to_f32(s16);
       for (int c = 0; c < j.group; ++c) {
         float v = sf == 0.f ? 0.f : std::nearbyint(x[c] / sf);
@@ -119,6 +119,7 @@ futx_status pack_host(const futx_dims* dims, futx_proj proj, const float* w, con
   ProjShape ps = proj_shape(*dims, proj);
   PackJob j{dims, proj, w, gain, (uint8_t*)packed, (uint16_t*)scales, ps.n, ps.k, dims->w_group,
             ps.k / kTileK};
+  std::memset(scales, 0, 2 * scale_count(ps.n, ps.k / kTileK, dims->w_group));  // padding
   // Rows of one 16-row tile share 32-bit words, so threads own whole tiles
   // (GATEUP: a logical tile maps to one physical tile).
   const int tiles = ps.n / kTileN;
@@ -150,7 +151,8 @@ futx_status unpack_host(const futx_dims* dims, futx_proj proj, const void* packe
   const uint16_t* sc = (const uint16_t*)scales;
   for (int n = 0; n < ps.n; ++n) {
     const int P = proj == FUTX_PROJ_GATEUP ? gateup_physical_row(n, dims->intermediate) : n;
-    std::memcpy(canon_scales + (size_t)n * ngroups, sc + (size_t)P * ngroups, 2 * (size_t)ngroups);
+    for (int g = 0; g < ngroups; ++g)
+      canon_scales[(size_t)n * ngroups + g] = sc[scale_index(P, g, kblocks, dims->w_group)];
     for (int c = 0; c < ps.k; c += 2) {
       uint8_t nib[2];
       for (int t = 0; t < 2; ++t) {

@@ -5,7 +5,7 @@ Weights: packed[nt][kb][L][16 bytes]; word s (bytes 4s..4s+3, little endian)
 of lane L holds row nt*16 + L%16, inputs kb*128 + 32 s + 8 (L // 16) + e;
 element e is stored as code + 8 in bits 3..6 of the word rotated left by
 4 (e // 2) + 16 (e % 2).  GATEUP physical tile 2t = gate rows 16t..,
-2t+1 = up rows 16t..
+2t+1 = up rows 16t..  Scales: see decode_scales.
 
 KV cache per (page, KV head): keys [tt][L][D/8 bytes] with token tt*16 + L%16
 and word s = channels 32 s + 8 (L//16) + e; values [tb][cg][L][16 bytes] with
@@ -34,6 +34,19 @@ def decode_weights(packed, n, k):
     codes = _nibbles(words)  # nt kb g i s e
     codes = codes.transpose(0, 3, 1, 4, 2, 5)  # nt i kb s g e
     return codes.reshape(n, k)
+
+
+def decode_scales(scales, n, k, group):
+    """Device-order fp16 group scales of an [n][k] projection -> [n_phys][k // group].
+
+    Blocked per 16-row tile and 8 K blocks of 128: [nt][kb // 8][i][slot], slot
+    = (kb % 8) * (128 // group) + (g % (128 // group)); the last block of 8 is
+    padded when k / 128 is not a multiple of 8."""
+    per_kb = 128 // group
+    kb8 = (k // 128 + 7) // 8
+    s = np.asarray(scales).view(np.uint16).reshape(n // 16, kb8, 16, 8 * per_kb)
+    s = s.transpose(0, 2, 1, 3).reshape(n, kb8 * 8 * per_kb)
+    return s[:, : k // group].view(np.float16)
 
 
 def gateup_logical_order(phys, inter):

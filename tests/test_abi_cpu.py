@@ -73,6 +73,9 @@ def test_argument_validation(fx):
 def test_sizes(fx):
     pb, sb = fx.futx_packed_sizes(W.LLAMA8B, "gateup")
     assert pb == 2 * 14336 * 4096 // 2 and sb == 2 * 14336 * 32 * 2
+    # scales are padded to whole blocks of 8 K blocks: K = 768 has 6
+    pb, sb = fx.futx_packed_sizes(W.TINY, "down")
+    assert pb == 256 * 768 // 2 and sb == 256 * 8 * 2 * 2
     cb, sb = fx.futx_kv_cache_sizes(W.LLAMA8B, 10)
     assert cb == 10 * 8 * 64 * 64 and sb == 10 * 8 * 64 * 2
     assert fx.futx_decode_workspace_size(W.LLAMA8B, 32, 8192) > fx.futx_decode_workspace_size(W.LLAMA8B, 1, 2048)
@@ -97,7 +100,7 @@ def test_host_pack_bit_exact_tiny(fx, proj):
     packed, scales = _host_pack(fx, d, proj, m, g)
     n, k = m.shape
     codes = layouts.decode_weights(packed, n, k)
-    sc = scales.view(np.float16).reshape(n, k // d.w_group)
+    sc = layouts.decode_scales(scales, n, k, d.w_group)
     if proj == "gateup":
         codes = layouts.gateup_logical_order(codes, d.intermediate)
         sc = layouts.gateup_logical_order(sc, d.intermediate)
@@ -123,7 +126,7 @@ def test_host_pack_edge_values(fx):
     codes = layouts.decode_weights(packed, 256, 256)
     want_q, want_s = oracle.quantize_weight_rtn(w, 64)
     np.testing.assert_array_equal(codes, want_q)
-    np.testing.assert_array_equal(scales.view(np.float16).reshape(256, 4).view(np.uint16), want_s.view(np.uint16))
+    np.testing.assert_array_equal(layouts.decode_scales(scales, 256, 256, 64).view(np.uint16), want_s.view(np.uint16))
     w[6, 0] = np.float32(1e6)  # max|w|/7 overflows fp16
     with pytest.raises(fx.FutxError) as e:
         _host_pack(fx, d, "o", w, None)
@@ -139,7 +142,7 @@ def test_host_pack_bit_exact_8b_slice(fx):
     codes = layouts.decode_weights(packed, 4096, 4096)
     want_q, want_s = oracle.quantize_weight_rtn(w, 128)
     np.testing.assert_array_equal(codes, want_q)
-    np.testing.assert_array_equal(scales.view(np.float16).reshape(4096, 32).view(np.uint16), want_s.view(np.uint16))
+    np.testing.assert_array_equal(layouts.decode_scales(scales, 4096, 4096, 128).view(np.uint16), want_s.view(np.uint16))
 
 
 def test_fold_head_matches_oracle(fx):
