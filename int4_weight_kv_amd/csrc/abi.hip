@@ -335,8 +335,7 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
   AttnPlan ap = attn_plan(B, d.n_kv_heads, max_context);
   STEP(launch_attention(ws.qrot, true, cached_lens, 1, block_table, max_pages_per_seq, B, nq, D,
                         ap, kvc, ws.apart, s));
-  STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act,
-                         term, nullptr, G, s));
+  STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act, term, s));
   // O projection + residual: h = x + O(o)
   STEP(gemm(w->o, H, nq * D, ws.act, 3, false, kEpiResid, x, ws.h, nullptr));
   // RMSNorm-2 + gate/up + SwiGLU -> bf16 activation
@@ -402,7 +401,7 @@ futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const ui
                             d.head_dim, ap, kv_cptrs(cache, d.n_kv_heads), ws.apart, s)) != hipSuccess)
     return hip_fail(e, "attention");
   if ((e = launch_attn_merge(ws.apart, lens, 0, batch, d.n_heads, d.head_dim, ap, d.had_block, out,
-                             nullptr, 0, nullptr, d.w_group, s)) != hipSuccess)
+                             nullptr, 0, s)) != hipSuccess)
     return hip_fail(e, "merge");
   return FUTX_OK;
 }

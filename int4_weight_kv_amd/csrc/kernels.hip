@@ -378,33 +378,42 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   const size_t head_bytes = (size_t)kPageSize * D / 2;
-  for (int blk = t0; blk < t1; blk += 32) {
-    const int page = block_table[(size_t)b * mpps + blk / kPageSize];
-    const int off = blk % kPageSize;  // 0 or 32
+  // One 64-token page per iteration: the codes and scales of its two
+  // 32-token blocks are loaded together, and the next page's table entry one
+  // page ahead, so no load waits on a page index just loaded.
+  struct Blk {
+    uint32_t kw[2][D / 32];
+    uint4 vw[D / 64];
+    uint2 k2[2], v2[2];
+  };
+  auto load_blk = [&](int page, int off, Blk& r) {
     const size_t hb_off = ((size_t)page * nkv + h) * head_bytes;
     const size_t sc_off = ((size_t)page * nkv + h) * kPageSize + off;
-    // key tiles (two 16-token tiles) and value tiles (D/64 channel groups)
-    uint32_t kw[2][D / 32];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint8_t* p = kv.k_codes + hb_off + (size_t)((off >> 4) + u) * (8 * D) + (size_t)lane * (D / 8);
       if constexpr (D == 128) {
         const uint4 v = *(const uint4*)p;
-        kw[u][0] = v.x; kw[u][1] = v.y; kw[u][2] = v.z; kw[u][3] = v.w;
+        r.kw[u][0] = v.x; r.kw[u][1] = v.y; r.kw[u][2] = v.z; r.kw[u][3] = v.w;
       } else {
         const uint2 v = *(const uint2*)p;
-        kw[u][0] = v.x; kw[u][1] = v.y;
+        r.kw[u][0] = v.x; r.kw[u][1] = v.y;
       }
     }
-    uint4 vw[D / 64];
 #pragma unroll
     for (int cg = 0; cg < D / 64; ++cg)
-      vw[cg] = *(const uint4*)(kv.v_codes + hb_off + (size_t)((off >> 5) * (D / 64) + cg) * 1024 + (size_t)lane * 16);
+      r.vw[cg] = *(const uint4*)(kv.v_codes + hb_off + (size_t)((off >> 5) * (D / 64) + cg) * 1024 + (size_t)lane * 16);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      r.k2[u] = *(const uint2*)(kv.k_scales + sc_off + 16 * u + 4 * grp);
+      r.v2[u] = *(const uint2*)(kv.v_scales + sc_off + 16 * u + 4 * grp);
+    }
+  };
+  auto compute_blk = [&](int blk, const Blk& rb) {
     float ks[2][4], vs[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint2 k2 = *(const uint2*)(kv.k_scales + sc_off + 16 * u + 4 * grp);
-      const uint2 v2 = *(const uint2*)(kv.v_scales + sc_off + 16 * u + 4 * grp);
+      const uint2 k2 = rb.k2[u], v2 = rb.v2[u];
       ks[u][0] = half_bits_to_f32(k2.x & 0xFFFF); ks[u][1] = half_bits_to_f32(k2.x >> 16);
       ks[u][2] = half_bits_to_f32(k2.y & 0xFFFF); ks[u][3] = half_bits_to_f32(k2.y >> 16);
       vs[u][0] = half_bits_to_f32(v2.x & 0xFFFF); vs[u][1] = half_bits_to_f32(v2.x >> 16);
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        const f16x8 kc = widen_word_exact_f16(kw[u][s]);
+        const f16x8 kc = widen_word_exact_f16(rb.kw[u][s]);
         d = mfma16h(kc, qh[s], d);
         d = mfma16h(kc, ql[s], d);
       }
@@ -468,12 +477,24 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
     for (int cg = 0; cg < D / 64; ++cg)
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        const f16x8 vc = widen_word_exact_f16(word_of(vw[cg], c4));
+        const f16x8 vc = widen_word_exact_f16(word_of(rb.vw[cg], c4));
         f32x4 dv = mfma16h(pah, vc, f32x4{0.f, 0.f, 0.f, 0.f});
         dv = mfma16h(pal, vc, dv);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
       }
+  };
+  const int* const bt = block_table + (size_t)b * mpps;
+  int page = bt[t0 / kPageSize];
+  for (int pt = t0; pt < t1; pt += kPageSize) {
+    const int page_next = bt[min(pt + kPageSize, t1 - 1) / kPageSize];
+    Blk r0, r1;
+    load_blk(page, pt % kPageSize, r0);
+    const bool two = pt + 32 < t1 && (pt % kPageSize) == 0;
+    load_blk(page, two ? 32 : pt % kPageSize, r1);
+    compute_blk(pt, r0);
+    if (two) compute_blk(pt + 32, r1);
+    page = page_next;
   }
   // finalize this chunk's partials
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
@@ -506,33 +527,82 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 // plus the exact group sums of that sum.  The attention output comes out of
 // a long fp32 reduction, so a single bf16 rounding here would flip on tiny
 // differences; three terms carry it at fp32 accuracy.
+// Cross-split softmax merge of one query head of one sequence, then the
+// inverse block rotation.  256 threads: thread t owns channel chunk t % (D/4)
+// (four channels) for the splits sp = t / (D/4) (mod 256 / (D/4)); all its
+// accumulator loads are issued before use, so the merge costs a few L2 round
+// trips, not one per split.
 template <int D>
-__global__ __launch_bounds__(128) void attn_merge_kernel(
+__global__ __launch_bounds__(256) void attn_merge_kernel(
     const float* __restrict__ apart, const int32_t* __restrict__ lens, int len_add, int nq,
     int chunk, int nsplit, int hb, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
-    size_t term_stride, float2* __restrict__ gsum, int G) {
-  const int i = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+    size_t term_stride) {
+  constexpr int NC = D / 4;       // float4 chunks per split
+  constexpr int PH = 256 / NC;    // split phases
+  constexpr int MAXW = 1024;      // splits held in LDS
+  __shared__ float s_w[MAXW];
+  __shared__ float4 s_acc[PH][NC];
+  __shared__ float s_red[4], s_l;
+  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int L = lens[b] + len_add;
-  const int nsp = (L + chunk - 1) / chunk;
+  const int nsp = min((L + chunk - 1) / chunk, nsplit);
   const float* base = apart + ((size_t)b * nq + i) * nsplit * (D + 2);
+  // running max over the splits
   float m = -INFINITY;
-  for (int sp = 0; sp < nsp; ++sp) m = fmaxf(m, base[sp * (D + 2)]);
-  float l = 0.f, a = 0.f;
-  for (int sp = 0; sp < nsp; ++sp) {
-    const float w = expf(base[sp * (D + 2)] - m);
-    l += w * base[sp * (D + 2) + 1];
-    a += w * base[sp * (D + 2) + 2 + c];
+  for (int sp = t; sp < nsp; sp += 256) m = fmaxf(m, base[(size_t)sp * (D + 2)]);
+  m = wave_max(m);
+  if (lane == 0) s_red[wv] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  float l = 0.f;
+  for (int sp = t; sp < nsp; sp += 256) {
+    const float w = expf(base[(size_t)sp * (D + 2)] - M);
+    if (sp < MAXW) s_w[sp] = w;
+    l += w * base[(size_t)sp * (D + 2) + 1];
   }
-  float o = l > 0.f ? a / l : 0.f;
+  l = wave_sum(l);
+  if (lane == 0) s_red[wv] = l;
+  __syncthreads();
+  if (t == 0) s_l = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  // weighted accumulators: 8 loads in flight per thread and batch
+  const int ch = t % NC, ph = t / NC;
+  float4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = ph; sp0 < nsp; sp0 += 8 * PH) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = min(sp0 + u * PH, nsp - 1);
+      v[u] = *(const float4*)(base + (size_t)sp * (D + 2) + 2 + 4 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = sp0 + u * PH;
+      const float w = sp < nsp ? (sp < MAXW ? s_w[sp] : expf(base[(size_t)sp * (D + 2)] - M)) : 0.f;
+      a.x = fmaf(w, v[u].x, a.x);
+      a.y = fmaf(w, v[u].y, a.y);
+      a.z = fmaf(w, v[u].z, a.z);
+      a.w = fmaf(w, v[u].w, a.w);
+    }
+  }
+  s_acc[ph][ch] = a;
+  __syncthreads();
+  if (t >= D) return;
+  // channel c = t: sum over the phases in a fixed order
+  const int c = t;
+  float o = 0.f;
+#pragma unroll
+  for (int p = 0; p < PH; ++p) o += ((const float*)&s_acc[p][c / 4])[c % 4];
+  const float ltot = s_l;
+  o = ltot > 0.f ? o / ltot : 0.f;
   // inverse rotation (the normalized Sylvester matrix is its own inverse)
-  const int lane = c & 63;
   for (int hop = 1; hop < hb; hop <<= 1) {
     const float p = __shfl_xor(o, hop, 64);
     o = (lane & hop) ? p - o : o + p;
   }
   o *= 1.0f / sqrtf((float)hb);
   if (out_f32) out_f32[((size_t)b * nq + i) * D + c] = o;
-  if (out_bf16) {
+  if (out_bf16) {  // o as three bf16 terms (hi + mid + lo), the O projection operand
     const uint16_t t0 = f32_to_bf16_bits(o);
     const float r1 = o - bf16_bits_to_f32(t0);
     const uint16_t t1 = f32_to_bf16_bits(r1);
@@ -541,21 +611,6 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(
     out_bf16[at] = t0;
     out_bf16[at + term_stride] = t1;
     out_bf16[at + 2 * term_stride] = t2;
-    if (!gsum) return;
-    // group sums (groups of G = 64 or 128 channels inside the head)
-    const double s = wave_sum_f64((double)bf16_bits_to_f32(t0) + (double)bf16_bits_to_f32(t1) +
-                                  (double)bf16_bits_to_f32(t2));
-    __shared__ double red[2];
-    if (lane == 0) red[c >> 6] = s;
-    __syncthreads();
-    if (c == 0) {
-      const int gpr = D / G;  // groups per head
-      for (int g2 = 0; g2 < gpr; ++g2) {
-        double t = 0.0;
-        for (int w = g2 * (G / 64); w < (g2 + 1) * (G / 64); ++w) t += red[w];
-        gsum[(size_t)(i * gpr + g2) * kMaxBatch + b] = split_f64(t);
-      }
-    }
   }
 }
 
@@ -652,13 +707,12 @@ hipError_t launch_attention(const void* q, bool q_f32, const int32_t* lens, int 
 
 hipError_t launch_attn_merge(const float* apart, const int32_t* lens, int len_add, int B, int nq,
                              int D, const AttnPlan& plan, int hb, float* out_f32,
-                             uint16_t* out_bf16, size_t term_stride, float2* gsum, int G,
-                             hipStream_t st) {
+                             uint16_t* out_bf16, size_t term_stride, hipStream_t st) {
   const dim3 grid(nq, B);
   if (D == 128)
-    attn_merge_kernel<128><<<grid, 128, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride, gsum, G);
+    attn_merge_kernel<128><<<grid, 256, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride);
   else
-    attn_merge_kernel<64><<<grid, 64, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride, gsum, G);
+    attn_merge_kernel<64><<<grid, 256, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }
