@@ -204,6 +204,29 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
                               const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Stages of futx_decode_block, in launch order. */
+#define FUTX_STAGE_QKV 0            /* RMSNorm-1 scale + QKV projection */
+#define FUTX_STAGE_ROTATE_APPEND 1  /* RoPE, block rotation, INT4 append, rotated queries */
+#define FUTX_STAGE_ATTENTION 2      /* split-sequence attention partials */
+#define FUTX_STAGE_MERGE 3          /* cross-split merge + inverse rotation */
+#define FUTX_STAGE_O 4              /* O projection + residual 1 */
+#define FUTX_STAGE_GATEUP 5         /* RMSNorm-2 scale + gate/up projection + SwiGLU */
+#define FUTX_STAGE_DOWN 6           /* down projection + residual 2 */
+#define FUTX_STAGE_COUNT 7
+
+/* Runs one stage of futx_decode_block with the same kernels, launch
+ * configuration and workspace, for per-kernel timing (same arguments, plus
+ * `stage` in [0, FUTX_STAGE_COUNT)).  A stage reads what the stages before it
+ * left in the workspace and cache, so call futx_decode_block once first for
+ * meaningful values; every stage is safe to repeat (the append rewrites the
+ * same slot, the projections recompute their outputs).  FUTX_E_ARG for a
+ * stage out of range; otherwise as futx_decode_block. */
+futx_status futx_decode_block_stage(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+                                    float* x, const int32_t* cached_lens, const int32_t* block_table,
+                                    int32_t max_pages_per_seq, int32_t max_context,
+                                    const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                                    int32_t stage, void* stream);
+
 /* ------------------------------------------------------ component entry points
  * Single steps of the block, for tests and profiling. */
 

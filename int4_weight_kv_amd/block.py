@@ -113,3 +113,9 @@ class DecodeRunner:
         """x: device fp32 [B][hidden], updated in place."""
         F.futx_decode_block(self.dims, layer.c_weights, self.batch, x, self.cached_lens, self.block_table,
                             self.mpps, self.max_context, cache.c_cache, self.workspace, self.ws_bytes, stream)
+
+    def stage(self, layer, cache, x, stage, stream=None):
+        """One stage of the block (futx_decode_block_stage), for timing."""
+        F.futx_decode_block_stage(self.dims, layer.c_weights, self.batch, x, self.cached_lens, self.block_table,
+                                  self.mpps, self.max_context, cache.c_cache, self.workspace, self.ws_bytes, stage,
+                                  stream)

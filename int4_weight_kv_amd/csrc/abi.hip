@@ -254,11 +254,12 @@ futx_status futx_decode_workspace_size(const futx_dims* dims, int32_t max_batch,
   return FUTX_OK;
 }
 
-futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
-                              float* x, const int32_t* cached_lens, const int32_t* block_table,
-                              int32_t max_pages_per_seq, int32_t max_context,
-                              const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+// stage < 0: every stage in order; otherwise that stage only
+static futx_status decode_block_impl(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+                                     float* x, const int32_t* cached_lens, const int32_t* block_table,
+                                     int32_t max_pages_per_seq, int32_t max_context,
+                                     const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                                     void* stream, int stage) {
   clear_error();
   futx_status st = check_dims(dims);
   if (st || (st = check_cache(cache))) return st;
@@ -283,6 +284,7 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
   const KVPtrsConst kvc = kv_cptrs(cache, d.n_kv_heads);
   const size_t term = (size_t)kMaxBatch * kmax(d);
   hipError_t e;
+  auto run = [stage](int k) { return stage < 0 || stage == k; };
 #define STEP(call)                                             \
   do {                                                         \
     if ((e = (call)) != hipSuccess) return hip_fail(e, #call); \
@@ -327,23 +329,48 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
     return hipErrorInvalidValue;
   };
   // RMSNorm-1 + QKV (the gain is folded into the weights; 1/r in the epilogue)
-  STEP(gemm(w->qkv, nqkv, H, x, 1, true, kEpiRms, nullptr, ws.qkv, nullptr));
+  if (run(FUTX_STAGE_QKV)) STEP(gemm(w->qkv, nqkv, H, x, 1, true, kEpiRms, nullptr, ws.qkv, nullptr));
   // RoPE, rotation, INT4 append of the new token; rotated fp32 queries
-  STEP(launch_post_qkv(ws.qkv, B, nq, D, cached_lens, block_table, max_pages_per_seq, d.had_block,
-                       d.rope_theta, ws.qrot, kv, s));
+  if (run(FUTX_STAGE_ROTATE_APPEND))
+    STEP(launch_post_qkv(ws.qkv, B, nq, D, cached_lens, block_table, max_pages_per_seq, d.had_block,
+                         d.rope_theta, ws.qrot, kv, s));
   // attention over positions 0..cached_lens[b]
   AttnPlan ap = attn_plan(B, d.n_kv_heads, max_context);
-  STEP(launch_attention(ws.qrot, true, cached_lens, 1, block_table, max_pages_per_seq, B, nq, D,
-                        ap, kvc, ws.apart, s));
-  STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act, term, s));
+  if (run(FUTX_STAGE_ATTENTION))
+    STEP(launch_attention(ws.qrot, true, cached_lens, 1, block_table, max_pages_per_seq, B, nq, D,
+                          ap, kvc, ws.apart, s));
+  if (run(FUTX_STAGE_MERGE))
+    STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act, term, s));
   // O projection + residual: h = x + O(o)
-  STEP(gemm(w->o, H, nq * D, ws.act, 3, false, kEpiResid, x, ws.h, nullptr));
+  if (run(FUTX_STAGE_O)) STEP(gemm(w->o, H, nq * D, ws.act, 3, false, kEpiResid, x, ws.h, nullptr));
   // RMSNorm-2 + gate/up + SwiGLU -> bf16 activation
-  STEP(gemm(w->gateup, 2 * I, H, ws.h, 1, true, kEpiSwiglu, nullptr, nullptr, ws.act));
+  if (run(FUTX_STAGE_GATEUP)) STEP(gemm(w->gateup, 2 * I, H, ws.h, 1, true, kEpiSwiglu, nullptr, nullptr, ws.act));
   // down projection + residual: x = h + down(act)
-  STEP(gemm(w->down, H, I, ws.act, 1, false, kEpiResid, ws.h, x, nullptr));
+  if (run(FUTX_STAGE_DOWN)) STEP(gemm(w->down, H, I, ws.act, 1, false, kEpiResid, ws.h, x, nullptr));
 #undef STEP
   return FUTX_OK;
+}
+
+futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+                              float* x, const int32_t* cached_lens, const int32_t* block_table,
+                              int32_t max_pages_per_seq, int32_t max_context,
+                              const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return decode_block_impl(dims, w, batch, x, cached_lens, block_table, max_pages_per_seq, max_context,
+                           cache, workspace, workspace_bytes, stream, -1);
+}
+
+futx_status futx_decode_block_stage(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+                                    float* x, const int32_t* cached_lens, const int32_t* block_table,
+                                    int32_t max_pages_per_seq, int32_t max_context,
+                                    const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
+                                    int32_t stage, void* stream) {
+  if (stage < 0 || stage >= FUTX_STAGE_COUNT) {
+    clear_error();
+    return fail(FUTX_E_ARG, "decode_block_stage: stage %d out of range", (int)stage);
+  }
+  return decode_block_impl(dims, w, batch, x, cached_lens, block_table, max_pages_per_seq, max_context,
+                           cache, workspace, workspace_bytes, stream, stage);
 }
 
 futx_status futx_int4_linear(const futx_dims* dims, futx_proj proj, const futx_qweight* w,

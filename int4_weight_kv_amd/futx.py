@@ -29,6 +29,11 @@ FUTX_E_HIP = -5
 FUTX_PROJ_QKV, FUTX_PROJ_O, FUTX_PROJ_GATEUP, FUTX_PROJ_DOWN = 0, 1, 2, 3
 PROJ_BY_NAME = {"qkv": 0, "o": 1, "gateup": 2, "down": 3}
 
+# stages of futx_decode_block (futx_decode_block_stage)
+(FUTX_STAGE_QKV, FUTX_STAGE_ROTATE_APPEND, FUTX_STAGE_ATTENTION, FUTX_STAGE_MERGE, FUTX_STAGE_O, FUTX_STAGE_GATEUP,
+ FUTX_STAGE_DOWN) = range(7)
+FUTX_STAGE_COUNT = 7
+
 FUTX_KV_ROPE = 1
 FUTX_KV_HADAMARD = 2
 
@@ -90,6 +95,8 @@ _SIGS = {
     "futx_decode_workspace_size": (_I32, [_D, _I32, _I32, _SZ]),
     "futx_decode_block": (_I32, [_D, ctypes.POINTER(futx_block_weights), _I32, _P, _P, _P, _I32, _I32,
                                  ctypes.POINTER(futx_kv_cache), _P, ctypes.c_size_t, _P]),
+    "futx_decode_block_stage": (_I32, [_D, ctypes.POINTER(futx_block_weights), _I32, _P, _P, _P, _I32, _I32,
+                                       ctypes.POINTER(futx_kv_cache), _P, ctypes.c_size_t, _I32, _P]),
     "futx_int4_linear": (_I32, [_D, _I32, ctypes.POINTER(futx_qweight), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
     "futx_decode_attention": (_I32, [_D, _I32, _P, _P, _P, _I32, _I32, ctypes.POINTER(futx_kv_cache), _P, _P,
                                      ctypes.c_size_t, _P]),
@@ -219,6 +226,15 @@ def futx_decode_block(dims, weights, batch, x, cached_lens, block_table, max_pag
                                                        int(max_pages_per_seq), int(max_context),
                                                        ctypes.byref(cache), _ptr(workspace), int(workspace_bytes),
                                                        _stream(stream)))
+
+
+def futx_decode_block_stage(dims, weights, batch, x, cached_lens, block_table, max_pages_per_seq, max_context,
+                            cache, workspace, workspace_bytes, stage, stream=None):
+    _check("futx_decode_block_stage",
+           _lib.futx_decode_block_stage(ctypes.byref(make_dims(dims)), ctypes.byref(weights), int(batch), _ptr(x),
+                                        _ptr(cached_lens), _ptr(block_table), int(max_pages_per_seq),
+                                        int(max_context), ctypes.byref(cache), _ptr(workspace),
+                                        int(workspace_bytes), int(stage), _stream(stream)))
 
 
 def futx_int4_linear(dims, proj, qweight, batch, act, out, workspace, workspace_bytes, stream=None):

@@ -70,6 +70,16 @@ def test_argument_validation(fx):
     assert "cache" in fx.futx_last_error()
 
 
+def test_decode_block_stage_range(fx):
+    """The stage number is checked before any pointer is used or kernel launched."""
+    for bad in (-1, fx.FUTX_STAGE_COUNT):
+        with pytest.raises(fx.FutxError) as e:
+            fx.futx_decode_block_stage(W.TINY, fx.futx_block_weights(), 1, None, None, None, 1, 1,
+                                       fx.futx_kv_cache(), None, 0, bad)
+        assert e.value.status == fx.FUTX_E_ARG
+        assert "stage" in fx.futx_last_error()
+
+
 def test_sizes(fx):
     pb, sb = fx.futx_packed_sizes(W.LLAMA8B, "gateup")
     assert pb == 2 * 14336 * 4096 // 2 and sb == 2 * 14336 * 32 * 2
