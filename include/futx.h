@@ -250,20 +250,30 @@ futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const ui
 
 /* --------------------------------------------------------- full decode step */
 
-/* x[b][:] = fp32(table[tokens[b]][:]) for a bf16 embedding table [vocab][hidden]. */
+/* x[b][:] = fp32(table[tokens[b]][:]) for a bf16 embedding table [vocab][hidden]
+ * (dev); tokens int32 [batch] (dev, trusted; out-of-range ids are clamped to
+ * [0, vocab)); x fp32 [batch][hidden] (dev).  batch 1..32. */
 futx_status futx_embed(int32_t hidden, int32_t vocab, const uint16_t* table_bf16,
                        const int32_t* tokens, int32_t batch, float* x, void* stream);
 
-/* LM head with the final RMSNorm: logits[b][v] = (sum_k bf16(x[b][k]) w[v][k])
- * / r_b with r_b = sqrt(mean_k x[b][k]^2 + eps), and top1[b] = the lowest
- * index of the largest logit.  w_bf16: [vocab][hidden] with the final norm
- * gain already folded in (see futx_fold_head).  batch 1..32. */
+/* LM head with the final RMSNorm [FP8 folding, ABS]: logits[b][v] =
+ * (sum_k bf16(x[b][k]) w[v][k]) / r_b with r_b = sqrt(mean_k x[b][k]^2 + eps),
+ * fp32 accumulation, and top1[b] = the lowest index of the largest logit.
+ *   w_bf16  [vocab][hidden] bf16 (dev, 16-byte aligned), final norm gain
+ *           already folded in (futx_fold_head).
+ *   x       fp32 [batch][hidden] (dev); logits fp32 [batch][vocab] (dev);
+ *           top1 int32 [batch] (dev).  batch 1..32.
+ *   workspace >= futx_lm_head_workspace_size(dims, vocab, batch) bytes (dev,
+ *           16-byte aligned), contents need not be initialized.
+ * FUTX_E_UNSUPPORTED unless dims->hidden is a multiple of 256. */
 futx_status futx_lm_head(const futx_dims* dims, int32_t vocab, const uint16_t* w_bf16,
                          int32_t batch, const float* x, float* logits, int32_t* top1,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of futx_lm_head. */
-futx_status futx_lm_head_workspace_size(int32_t vocab, int32_t max_batch, size_t* bytes);
+/* Workspace bytes of futx_lm_head for up to `max_batch` rows (1..32).
+ * FUTX_E_UNSUPPORTED unless dims->hidden is a multiple of 256. */
+futx_status futx_lm_head_workspace_size(const futx_dims* dims, int32_t vocab, int32_t max_batch,
+                                        size_t* bytes);
 
 /* Host-side fold of the final norm gain into the bf16 LM head:
  * out[v][k] = bf16(fp32(w[v][k]) * gain[k]) (round to nearest even). */

@@ -119,3 +119,43 @@ class DecodeRunner:
         F.futx_decode_block_stage(self.dims, layer.c_weights, self.batch, x, self.cached_lens, self.block_table,
                                   self.mpps, self.max_context, cache.c_cache, self.workspace, self.ws_bytes, stage,
                                   stream)
+
+
+class DecodeHead:
+    """Embedding table and LM head (final norm gain folded in, bf16) on the device."""
+
+    def __init__(self, dims, emb_values, head_values, final_gain, max_batch, device="cuda"):
+        torch = _torch()
+        self.dims = dims
+        self.vocab, hidden = emb_values.shape
+        emb_bits = (np.ascontiguousarray(emb_values, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        head_bits = (np.ascontiguousarray(head_values, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        folded = np.empty_like(head_bits)
+        F.futx_fold_head(self.vocab, hidden, head_bits, final_gain, folded)
+        self.emb = torch.from_numpy(emb_bits.view(np.int16)).to(device)
+        self.head = torch.from_numpy(folded.view(np.int16)).to(device)
+        self.ws_bytes = F.futx_lm_head_workspace_size(dims, self.vocab, max_batch)
+        self.workspace = device_buffer(self.ws_bytes, device)
+
+    def embed(self, tokens, x, stream=None):
+        F.futx_embed(self.dims.hidden, self.vocab, self.emb, tokens, tokens.shape[0], x, stream)
+
+    def lm_head(self, x, logits, top1, stream=None):
+        F.futx_lm_head(self.dims, self.vocab, self.head, x.shape[0], x, logits, top1, self.workspace,
+                       self.ws_bytes, stream)
+
+
+class DecodeStep:
+    """A full decode step: embedding, the blocks in order, final norm + LM head."""
+
+    def __init__(self, dims, layers, caches, head: DecodeHead, runner: DecodeRunner):
+        self.dims, self.layers, self.caches, self.head, self.runner = dims, layers, caches, head, runner
+
+    def step(self, tokens, x, logits, top1, stream=None, progress=None):
+        """tokens: device int32 [B]; x: device fp32 [B][hidden] scratch; logits fp32 [B][vocab]; top1 int32 [B]."""
+        self.head.embed(tokens, x, stream)
+        for i, (layer, cache) in enumerate(zip(self.layers, self.caches)):
+            self.runner.decode(layer, cache, x, stream)
+            if progress is not None:
+                progress(i)
+        self.head.lm_head(x, logits, top1, stream)

@@ -7,6 +7,7 @@
 #include <vector>
 
 #include "gemm.h"
+#include "head.h"
 #include "internal.h"
 #include "kernels.h"
 
@@ -436,19 +437,43 @@ futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const ui
 futx_status futx_embed(int32_t hidden, int32_t vocab, const uint16_t* table_bf16,
                        const int32_t* tokens, int32_t batch, float* x, void* stream) {
   clear_error();
-  return fail(FUTX_E_UNSUPPORTED, "embed: not built yet");
+  if (hidden <= 0 || vocab <= 0) return fail(FUTX_E_ARG, "embed: hidden and vocab must be positive");
+  if (batch < 1 || batch > kMaxBatch) return fail(FUTX_E_ARG, "embed: batch must be 1..32");
+  if (!table_bf16 || !tokens || !x) return fail(FUTX_E_ARG, "embed: null pointer");
+  hipError_t e = launch_embed(table_bf16, tokens, vocab, hidden, batch, x, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "embed");
+  return FUTX_OK;
+}
+
+futx_status futx_lm_head_workspace_size(const futx_dims* dims, int32_t vocab, int32_t max_batch, size_t* bytes) {
+  clear_error();
+  futx_status st = check_dims(dims);
+  if (st) return st;
+  if (vocab <= 0 || max_batch < 1 || max_batch > kMaxBatch || !bytes)
+    return fail(FUTX_E_ARG, "lm_head_workspace_size: bad arguments");
+  if (!head_shape_ok(dims->hidden)) return fail(FUTX_E_UNSUPPORTED, "lm_head: hidden must be a multiple of 256");
+  *bytes = head_ws(dims->hidden, vocab, max_batch, nullptr).bytes;
+  return FUTX_OK;
 }
 
 futx_status futx_lm_head(const futx_dims* dims, int32_t vocab, const uint16_t* w_bf16,
                          int32_t batch, const float* x, float* logits, int32_t* top1,
                          void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  return fail(FUTX_E_UNSUPPORTED, "lm_head: not built yet");
-}
-
-futx_status futx_lm_head_workspace_size(int32_t vocab, int32_t max_batch, size_t* bytes) {
-  clear_error();
-  return fail(FUTX_E_UNSUPPORTED, "lm_head: not built yet");
+  futx_status st = check_dims(dims);
+  if (st) return st;
+  if (vocab <= 0) return fail(FUTX_E_ARG, "lm_head: vocab must be positive");
+  if (batch < 1 || batch > kMaxBatch) return fail(FUTX_E_ARG, "lm_head: batch must be 1..32");
+  if (!w_bf16 || !x || !logits || !top1 || !workspace) return fail(FUTX_E_ARG, "lm_head: null pointer");
+  if (((uintptr_t)w_bf16 | (uintptr_t)workspace) & 15) return fail(FUTX_E_ARG, "lm_head: pointers must be 16-byte aligned");
+  if (!head_shape_ok(dims->hidden)) return fail(FUTX_E_UNSUPPORTED, "lm_head: hidden must be a multiple of 256");
+  const HeadWs ws = head_ws(dims->hidden, vocab, batch, (char*)workspace);
+  if (ws.bytes > workspace_bytes)
+    return fail(FUTX_E_WORKSPACE, "lm_head: workspace %zu < %zu bytes", workspace_bytes, ws.bytes);
+  hipError_t e = launch_lm_head(w_bf16, x, batch, dims->hidden, vocab, dims->rms_eps, ws, logits, top1,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "lm_head");
+  return FUTX_OK;
 }
 
 futx_status futx_fold_head(int32_t vocab, int32_t hidden, const uint16_t* w_bf16_host,

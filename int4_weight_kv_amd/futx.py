@@ -102,7 +102,7 @@ _SIGS = {
                                      ctypes.c_size_t, _P]),
     "futx_embed": (_I32, [_I32, _I32, _P, _P, _I32, _P, _P]),
     "futx_lm_head": (_I32, [_D, _I32, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "futx_lm_head_workspace_size": (_I32, [_I32, _I32, _SZ]),
+    "futx_lm_head_workspace_size": (_I32, [_D, _I32, _I32, _SZ]),
     "futx_fold_head": (_I32, [_I32, _I32, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -258,10 +258,11 @@ def futx_embed(hidden, vocab, table_bf16, tokens, batch, x, stream=None):
                                          _ptr(x), _stream(stream)))
 
 
-def futx_lm_head_workspace_size(vocab, max_batch):
+def futx_lm_head_workspace_size(dims, vocab, max_batch):
     b = ctypes.c_size_t()
-    _check("futx_lm_head_workspace_size", _lib.futx_lm_head_workspace_size(int(vocab), int(max_batch),
-                                                                           ctypes.byref(b)))
+    _check("futx_lm_head_workspace_size",
+           _lib.futx_lm_head_workspace_size(ctypes.byref(make_dims(dims)), int(vocab), int(max_batch),
+                                            ctypes.byref(b)))
     return b.value
 
 

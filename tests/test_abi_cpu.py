@@ -80,6 +80,23 @@ def test_decode_block_stage_range(fx):
         assert "stage" in fx.futx_last_error()
 
 
+def test_lm_head_workspace_and_validation(fx):
+    n = fx.futx_lm_head_workspace_size(W.LLAMA8B, 128256, 16)
+    assert n >= 4 * 16 * 128256 * 4  # fp32 partials of four K splits
+    assert fx.futx_lm_head_workspace_size(W.LLAMA8B, 128256, 32) >= n
+    odd = W.Dims(384, 4, 2, 64, 768, 64, 32)  # hidden not a multiple of 256
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_lm_head_workspace_size(odd, 1000, 1)
+    assert e.value.status == fx.FUTX_E_UNSUPPORTED
+    for bad in (0, 33):
+        with pytest.raises(fx.FutxError) as e:
+            fx.futx_lm_head(W.LLAMA8B, 1000, None, bad, None, None, None, None, 0)
+        assert e.value.status == fx.FUTX_E_ARG
+    with pytest.raises(fx.FutxError) as e:
+        fx.futx_embed(4096, 1000, None, None, 1, None)
+    assert e.value.status == fx.FUTX_E_ARG
+
+
 def test_sizes(fx):
     pb, sb = fx.futx_packed_sizes(W.LLAMA8B, "gateup")
     assert pb == 2 * 14336 * 4096 // 2 and sb == 2 * 14336 * 32 * 2
