@@ -277,3 +277,11 @@ def test_block_8b():
 @pytest.mark.parametrize("batch", [1, 4, 8, 16, 32])
 def test_block_8b_ragged_outliers(batch):
     _check_block(BlockCase(W.llama8b_ragged(batch)), reps=1)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("batch", [1, 4, 8, 16, 32])
+def test_block_70b(batch):
+    """Llama-3-70B-shape block (hidden 8192, 64/8 heads, intermediate 28672),
+    4096 cached tokens per sequence."""
+    _check_block(BlockCase(W.llama70b(batch)), reps=1)
