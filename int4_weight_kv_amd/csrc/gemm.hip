@@ -36,13 +36,15 @@
 
 namespace futx {
 
-// Register budget: three waves per SIMD for G = 128 and a batch of up to 16,
-// otherwise two or one.
+// Register budget: at most three waves per SIMD (more would make the
+// compiler spill the prologue's staging registers), three for G = 128 and a
+// batch of up to 16, otherwise two or one.
 template <int G, int NF, int NR, int NT, bool F32, int EPI, int PAIR>
-__global__ __launch_bounds__(256, (NF == 1 && G == 128) ? 2 : 1) void int4_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, (NF == 1 && G == 128) ? 2 : 1)
+__attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
   constexpr int NTW = PAIR ? 2 : 1;                  // weight tiles per item (gate + up)
   constexpr int CHK = (PAIR || NF == 2) ? 4 : 8;     // K blocks per chunk and wave
-  constexpr int MAXP = 4;                            // activation passes held in registers
+  constexpr int MAXP = (!F32 && NT == 1) ? 8 : 4;    // activation passes held in registers
   extern __shared__ __align__(16) uint8_t s_dyn[];
   // LDS (gemm_lds_layout): activation range [NT][B][row] bf16 | group sums
   // [B][ngr] float2 | group sums of squares [B][ngr] | partials
@@ -130,9 +132,14 @@ __global__ __launch_bounds__(256, (NF == 1 && G == 128) ? 2 : 1) void int4_gemm_
       for (int t = 0; t < NT; ++t) r[t] = *(const uint4*)((const uint16_t*)a.act + t * a.term_stride + src);
     }
   };
-  auto act_store = [&](int p, const ActRegs& r) {
+  // valid == false: the pass is past the end (registers hold a repeated
+  // pass) and nothing is written; a flag rather than a branch around the
+  // call, since a guarded unrolled loop becomes an early-exit loop with a
+  // dynamically indexed register array (scratch)
+  auto act_store = [&](int p, const ActRegs& r, bool valid) {
+    p = valid ? p : 0;
     const int b = p / ppr, e = (p - b * ppr) * 512 + lane * 8;
-    const bool ok = e < qk;
+    const bool ok = valid && e < qk;
     const int kl = (q0 - kb0) * 128 + e;  // offset in the workgroup's K range
     double gs = 0.0;
     float sq = 0.f;
@@ -286,9 +293,12 @@ __global__ __launch_bounds__(256, (NF == 1 && G == 128) ? 2 : 1) void int4_gemm_
     // scales first (oldest loads: waiting for them does not wait for
     // weights); unconditional loads with clamped indices, since
     // conditionally assigned register arrays are placed in scratch
-    uint4 sr[MAXS];
-#pragma unroll
-    for (int k = 0; k < MAXS; ++k) sr[k] = *scl_src(min(k * 256 + tid, npieces - 1));
+    // four named registers, not an array: the compiler cannot index them
+    static_assert(MAXS == 4, "four scale pieces per thread");
+    const uint4 sr0 = *scl_src(min(tid, npieces - 1));
+    const uint4 sr1 = *scl_src(min(256 + tid, npieces - 1));
+    const uint4 sr2 = *scl_src(min(512 + tid, npieces - 1));
+    const uint4 sr3 = *scl_src(min(768 + tid, npieces - 1));
     if (npass <= MAXP) {
       ActRegs r[MAXP];
 #pragma unroll
@@ -296,20 +306,23 @@ __global__ __launch_bounds__(256, (NF == 1 && G == 128) ? 2 : 1) void int4_gemm_
       load_chunk(wA, 0);
       if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
 #pragma unroll
-      for (int p = 0; p < MAXP; ++p)
-        if (p < npass) act_store(p, r[p]);
+      for (int p = 0; p < MAXP; ++p) act_store(p, r[p], p < npass);
     } else {
-      for (int p = 0; p < npass; ++p) {
-        ActRegs r;
-        act_load(p, r);
-        act_store(p, r);
+      // MAXP passes per round trip (loads clamped, stores guarded)
+      for (int p0 = 0; p0 < npass; p0 += MAXP) {
+        ActRegs r[MAXP];
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) act_load(min(p0 + p, npass - 1), r[p]);
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) act_store(p0 + p, r[p], p0 + p < npass);
       }
       load_chunk(wA, 0);
       if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
     }
-#pragma unroll
-    for (int k = 0; k < MAXS; ++k)
-      if (k * 256 + tid < npieces) ((uint4*)s_scl)[k * 256 + tid] = sr[k];
+    if (tid < npieces) ((uint4*)s_scl)[tid] = sr0;
+    if (256 + tid < npieces) ((uint4*)s_scl)[256 + tid] = sr1;
+    if (512 + tid < npieces) ((uint4*)s_scl)[512 + tid] = sr2;
+    if (768 + tid < npieces) ((uint4*)s_scl)[768 + tid] = sr3;
     // pieces beyond the registers (the planner avoids this; correct but slow)
     for (int q = MAXS * 256 + tid; q < npieces; q += 256) ((uint4*)s_scl)[q] = *scl_src(q);
     zero_acc();

@@ -106,15 +106,22 @@ __global__ __launch_bounds__(128) void swiglu_kernel(const float* __restrict__ p
 
 // ---------------------------------------------------------------- KV append
 
-// cos / sin of the RoPE angle pos * theta^(-2i/d), computed in fp64 so that
-// long positions keep full fp32 accuracy.
+// cos / sin of the RoPE angle pos * theta^(-2i/d).  The angle is formed and
+// reduced modulo 2 pi in fp64 (Cody-Waite with a two-part 2 pi), so long
+// positions keep full accuracy; fp64 sin / cos of the reduced angle in
+// [-pi, pi] then cost no large-argument reduction, and the fp32 results are
+// the correctly rounded values but for rare double-rounding cases.
 __device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float* c, float* s) {
-  const double inv = pow((double)theta, -2.0 * (double)i / (double)d);
+  const double inv = exp2(-2.0 * (double)i / (double)d * log2((double)theta));
   const double ang = (double)pos * inv;
+  constexpr double kTwoPiHi = 6.28318530717958623200e+00;  // 2 pi rounded to double
+  constexpr double kTwoPiLo = 2.44929359829470635445e-16;  // 2 pi - kTwoPiHi
+  const double k = rint(ang * (1.0 / kTwoPiHi));
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
   double sn, cs;
-  sincos(ang, &sn, &cs);
-  *c = (float)cs;
+  sincos(r, &sn, &cs);  // |r| <= pi: no large-argument reduction left
   *s = (float)sn;
+  *c = (float)cs;
 }
 
 // Rotate-half RoPE of one head held as channel c = lane + 64 j.

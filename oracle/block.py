@@ -173,9 +173,16 @@ def history_fill(cache, k_pre, v, positions, dims):
     cache.v_codes[pos], cache.v_scales[pos] = vc, vs
 
 
-def decode_block(x, weights, caches, lens, dims, diag=None):
+def decode_block(x, weights, caches, lens, dims, diag=None, kv_hook=None):
     """O4-O13 for a batch.  ``x`` fp32 [B][H]; ``caches`` one LogicalKVCache per
-    sequence (the new token is appended at ``lens[b]``).  Returns y fp64 [B][H]."""
+    sequence (the new token is appended at ``lens[b]``).  Returns y fp64 [B][H].
+
+    ``kv_hook`` (tests only; None leaves the arithmetic as stated): called as
+    kv_hook(b, kc, ks, vc, vs, k_rot, v_rot) with the new token's codes and
+    scales (O8) and the fp64 rotated k, v they were quantized from; it returns
+    the codes and scales to append.  A test uses it to continue with an
+    implementation's choice where a value sits on a rounding boundary, after
+    checking that the choice is one of the two valid ones."""
     x = np.asarray(x, np.float64)
     bsz = x.shape[0]
     nq, nkv, d = dims.n_heads, dims.n_kv_heads, dims.head_dim
@@ -196,6 +203,8 @@ def decode_block(x, weights, caches, lens, dims, diag=None):
         # O8
         kc, ks = quantize_kv_token(k_rot.astype(np.float32))
         vc, vs = quantize_kv_token(v_rot.astype(np.float32))
+        if kv_hook is not None:
+            kc, ks, vc, vs = kv_hook(b, kc, ks, vc, vs, k_rot, v_rot)
         caches[b].write(pos, kc, ks, vc, vs)
         # O9
         k_hat, v_hat = caches[b].dequant(pos + 1)
