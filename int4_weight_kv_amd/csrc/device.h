@@ -1,6 +1,8 @@
 // Device helpers for the gfx950 kernels (wave64, bf16 MFMA).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -131,6 +133,46 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Cross-lane moves within a row of 16 lanes through the DPP modifier (a VALU
+// operand form: no LDS round trip).  Controls: quad_perm [1,0,3,2] and
+// [2,3,0,1] swap neighbours at distance 1 and 2; row_half_mirror maps lane i
+// of each 8 to 7 - i, row_mirror lane i of 16 to 15 - i.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8 or 16); every
+// lane of a group gets the group's sum.  After the two quad steps all lanes
+// of a quad hold its sum, so each mirror step adds the partner quad's (or
+// half-row's) sum: the same pairing as an xor butterfly, hence the same value
+// in every lane.
+template <int N, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+  auto mv = [](auto ctrl, T x) -> T {
+    if constexpr (sizeof(T) == 8) return dpp_f64<decltype(ctrl)::value>(x);
+    else return dpp_f32<decltype(ctrl)::value>(x);
+  };
+  if constexpr (N >= 2) v += mv(std::integral_constant<int, kDppQuadXor1>{}, v);
+  if constexpr (N >= 4) v += mv(std::integral_constant<int, kDppQuadXor2>{}, v);
+  if constexpr (N >= 8) v += mv(std::integral_constant<int, kDppHalfMirror>{}, v);
+  if constexpr (N >= 16) v += mv(std::integral_constant<int, kDppMirror>{}, v);
   return v;
 }
 

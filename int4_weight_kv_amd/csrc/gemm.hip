@@ -83,6 +83,16 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
   const int nchunks = (it1 - it0) * cpi;
   if (nchunks == 0) return;  // the whole workgroup: before any barrier
 
+  // Residual of the first write-out pass, loaded before anything else so the
+  // epilogue does not start a dependent round trip (oldest load: waiting for
+  // it never waits for a weight load).  Clamped, unconditional.
+  float resid_pf = 0.f;
+  if constexpr (EPI == kEpiResid) {
+    const int idx = min(tid, (it1 - it0) * B * 16 - 1);
+    const int il = idx / (B * 16), rem = idx - il * B * 16;
+    resid_pf = a.resid[(size_t)(rem >> 4) * a.N + (it0 + il) * 16 + (rem & 15)];
+  }
+
   // ---- weights: the main loop issues weight loads only (scales come from LDS)
   uint4 wA[CHK][NTW], wB[CHK][NTW];
   // Out-of-range K blocks of a chunk re-read the quarter's first block and
@@ -132,14 +142,14 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
       for (int t = 0; t < NT; ++t) r[t] = *(const uint4*)((const uint16_t*)a.act + t * a.term_stride + src);
     }
   };
-  // valid == false: the pass is past the end (registers hold a repeated
-  // pass) and nothing is written; a flag rather than a branch around the
-  // call, since a guarded unrolled loop becomes an early-exit loop with a
-  // dynamically indexed register array (scratch)
+  // valid == false (wave-uniform): the pass is past the end (registers hold
+  // a repeated pass) and is skipped.  Callers derive the flag so that the
+  // compiler cannot turn the guarded unrolled loop into an early-exit loop
+  // over a dynamically indexed register array (scratch).
   auto act_store = [&](int p, const ActRegs& r, bool valid) {
-    p = valid ? p : 0;
+    if (!valid) return;
     const int b = p / ppr, e = (p - b * ppr) * 512 + lane * 8;
-    const bool ok = valid && e < qk;
+    const bool ok = e < qk;
     const int kl = (q0 - kb0) * 128 + e;  // offset in the workgroup's K range
     double gs = 0.0;
     float sq = 0.f;
@@ -161,11 +171,8 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
         gs += (double)bf16_bits_to_f32(w4[c] & 0xFFFF) + (double)bf16_bits_to_f32(w4[c] >> 16);
     }
     // a weight group is G / 8 consecutive lanes
-#pragma unroll
-    for (int o = 1; o < G / 8; o <<= 1) {
-      gs += __shfl_xor(gs, o, 64);
-      if constexpr (F32) sq += __shfl_xor(sq, o, 64);
-    }
+    gs = group_sum<G / 8>(gs);
+    if constexpr (F32) sq = group_sum<G / 8>(sq);
     if (ok && (lane % (G / 8)) == 0) {
       s_gsum[(size_t)b * ngr + kl / G] = split_f64(gs);
       if constexpr (F32) s_sqg[(size_t)b * ngr + kl / G] = sq;
@@ -299,14 +306,32 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
     const uint4 sr1 = *scl_src(min(256 + tid, npieces - 1));
     const uint4 sr2 = *scl_src(min(512 + tid, npieces - 1));
     const uint4 sr3 = *scl_src(min(768 + tid, npieces - 1));
+    // Unconditional stores at the same clamped indices: threads past the
+    // last piece rewrite it with the value they loaded from it.  No branch
+    // may separate these stores from their loads, since the compiler's
+    // memory-counter wait at a control-flow join falls back to waiting for
+    // every load in flight (the weights included).
+    auto store_scales = [&]() {
+      ((uint4*)s_scl)[min(tid, npieces - 1)] = sr0;
+      ((uint4*)s_scl)[min(256 + tid, npieces - 1)] = sr1;
+      ((uint4*)s_scl)[min(512 + tid, npieces - 1)] = sr2;
+      ((uint4*)s_scl)[min(768 + tid, npieces - 1)] = sr3;
+    };
     if (npass <= MAXP) {
+      // passes past npass repeat a valid one and are skipped; the mask is
+      // opaque to the compiler so the unrolled loop keeps static register
+      // indices (a bound it could see turns into a loop over a dynamically
+      // indexed array in scratch)
+      uint32_t live_pass = (1u << npass) - 1u;
+      asm volatile("" : "+s"(live_pass));
       ActRegs r[MAXP];
 #pragma unroll
       for (int p = 0; p < MAXP; ++p) act_load(min(p, npass - 1), r[p]);  // clamped; see above
       load_chunk(wA, 0);
       if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
 #pragma unroll
-      for (int p = 0; p < MAXP; ++p) act_store(p, r[p], p < npass);
+      for (int p = 0; p < MAXP; ++p) act_store(p, r[p], (live_pass >> p) & 1u);
+      store_scales();
     } else {
       // MAXP passes per round trip (loads clamped, stores guarded)
       for (int p0 = 0; p0 < npass; p0 += MAXP) {
@@ -316,13 +341,10 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int p = 0; p < MAXP; ++p) act_store(p0 + p, r[p], p0 + p < npass);
       }
+      store_scales();
       load_chunk(wA, 0);
       if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
     }
-    if (tid < npieces) ((uint4*)s_scl)[tid] = sr0;
-    if (256 + tid < npieces) ((uint4*)s_scl)[256 + tid] = sr1;
-    if (512 + tid < npieces) ((uint4*)s_scl)[512 + tid] = sr2;
-    if (768 + tid < npieces) ((uint4*)s_scl)[768 + tid] = sr3;
     // pieces beyond the registers (the planner avoids this; correct but slow)
     for (int q = MAXS * 256 + tid; q < npieces; q += 256) ((uint4*)s_scl)[q] = *scl_src(q);
     zero_acc();
@@ -377,7 +399,8 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
     } else if constexpr (EPI == kEpiRms) {
       a.out[(size_t)tok * a.N + n] = o * (1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps));
     } else if constexpr (EPI == kEpiResid) {
-      a.out[(size_t)tok * a.N + n] = a.resid[(size_t)tok * a.N + n] + o;
+      const float rv = idx == tid ? resid_pf : a.resid[(size_t)tok * a.N + n];
+      a.out[(size_t)tok * a.N + n] = rv + o;
     } else {  // kEpiSwiglu: u = 0 gate rows, u = 1 up rows of logical column n
       const float invr = 1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps);
       const float g = o * invr, up = s_out[((il * NTW + PAIR) * B + tok) * 16 + cc] * invr;
@@ -462,7 +485,10 @@ hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi
 #define FUTX_G(GG, NF, NR, NT, F32, EPI, PR) \
   do {                                   \
     auto k_ = int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR>; \
-    if (lds > 64 * 1024) hipFuncSetAttribute((const void*)k_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (lds > 64 * 1024) {                                                  \
+      const hipError_t e_ = hipFuncSetAttribute((const void*)k_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e_ != hipSuccess) return e_;                                      \
+    }                                                                       \
     k_<<<grid, block, lds, st>>>(a); \
   } while (0)
 #define FUTX_NF(GG, NT, F32, EPI, PR) \
