@@ -3,6 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b-b1]
                     [--phase all|block|dominant|copy]
 
+Workloads: 8b-b<B>, 8b-ragged-b<B>, 70b-b<B>, tiny-b<B> (one block), and
+step-b<B> (the full 32-layer step, its own JSON line in ms/step).
+
 One step = one decode block (RMSNorm -> INT4 QKV -> RoPE + Hadamard + INT4
 append -> split-sequence attention -> O + residual -> RMSNorm -> INT4
 gate/up + SwiGLU -> INT4 down + residual) over one batch of synthetic inputs
@@ -58,6 +61,9 @@ def workload_by_name(name):
         return W.llama70b(b), "Llama-3-70B-shape decode block, 4096 cached tokens"
     if kind == "tiny":
         return W.tiny(b), "tiny Llama-style decode block, 128 cached tokens"
+    if kind == "step":
+        return (W.llama8b_full_step(b), "full 32-layer Llama-3.1-8B-shape decode step (embedding, 32 INT4 blocks, "
+                "bf16 LM head vocab 128256 + top-1), 8192 cached tokens, outlier keys")
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -163,6 +169,76 @@ def cpu_baseline(wl, lens, budget_s=15.0):
     }
 
 
+def step_bytes_full(wl, lens):
+    """Algorithmic bytes of a full step: every block's bytes, the embedding
+    rows read (bf16), the bf16 LM head, the logits written (fp32)."""
+    d = wl.dims
+    return (wl.n_layers * algorithmic_bytes(d, lens) + 2 * wl.batch * d.hidden +
+            2 * wl.vocab * d.hidden + 4 * wl.batch * wl.vocab)
+
+
+def full_step_phase(args, wl, desc):
+    """Times the full decode step (32 distinct layers: the weights alone,
+    3.6 GB, exceed the Infinity Cache) replayed from one graph."""
+    import torch
+
+    from int4_weight_kv_amd import block as DB
+    from int4_weight_kv_amd import workload as W
+
+    d = wl.dims
+    lens = wl.cached_lengths(0)
+    layout = W.page_layout(wl, lens, extra_tokens=1, seed=0)
+    layers, caches = [], []
+    for li in range(wl.n_layers):
+        w = W.block_weights(wl, li)
+        layers.append(DB.DeviceLayer(d, w))
+        del w
+        cache = DB.DeviceKVCache(d, layout.num_pages)
+        for b, L in enumerate(lens):
+            k, v = W.history(wl, li, b, int(L))
+            DB.fill_history(cache, k, v, layout, b)
+        caches.append(cache)
+        print(f"[bench] layer {li} set up", file=sys.stderr, flush=True)
+    emb, head, gain = W.lm_tables(wl)
+    dh = DB.DecodeHead(d, emb, head, gain, wl.batch)
+    del emb, head
+    runner = DB.DecodeRunner(d, wl.batch, lens, layout.block_table)
+    step = DB.DecodeStep(d, layers, caches, dh, runner)
+    tok = torch.from_numpy(W.tokens(wl)).cuda()
+    x = torch.empty((wl.batch, d.hidden), dtype=torch.float32, device="cuda")
+    logits = torch.empty((wl.batch, wl.vocab), dtype=torch.float32, device="cuda")
+    top1 = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step.step(tok, x, logits, top1)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step.step(tok, x, logits, top1)
+    with torch.cuda.stream(stream):
+        g.replay()
+    stream.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        stop.record(stream)
+    stop.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = step_bytes_full(wl, lens)
+    print(json.dumps({
+        "metric": "full decode step ms/step (32 INT4 blocks + embedding + bf16 LM head)",
+        "value": round(ms, 4), "unit": "ms/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": desc, "batch": int(wl.batch), "cached_tokens": int(lens[0]), "graph_replay": True,
+                   "step_bytes": int(nbytes), "step_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }), flush=True)
+
+
 def copy_phase(torch, reps):
     """A plain device copy of COPY_BYTES, for the counter calibration."""
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -203,6 +279,9 @@ def main():
     from int4_weight_kv_amd import workload as W
 
     wl, desc = workload_by_name(args.workload)
+    if args.workload.startswith("step-"):
+        full_step_phase(args, wl, desc)
+        return
     d = wl.dims
     lens = wl.cached_lengths(0)
     layout = W.page_layout(wl, lens, extra_tokens=1, seed=0)

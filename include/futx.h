@@ -206,8 +206,9 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
 
 /* Stages of futx_decode_block, in launch order. */
 #define FUTX_STAGE_QKV 0            /* RMSNorm-1 scale + QKV projection */
-#define FUTX_STAGE_ROTATE_APPEND 1  /* RoPE, block rotation, INT4 append, rotated queries */
-#define FUTX_STAGE_ATTENTION 2      /* split-sequence attention partials */
+#define FUTX_STAGE_ROTATE_APPEND 1  /* (inside the attention kernel: launches nothing) */
+#define FUTX_STAGE_ATTENTION 2      /* one kernel: RoPE, block rotation and INT4 append of the new
+                                       token, rotated queries, split-sequence attention partials */
 #define FUTX_STAGE_MERGE 3          /* cross-split merge + inverse rotation */
 #define FUTX_STAGE_O 4              /* O projection + residual 1 */
 #define FUTX_STAGE_GATEUP 5         /* RMSNorm-2 scale + gate/up projection + SwiGLU */

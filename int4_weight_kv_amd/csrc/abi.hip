@@ -81,7 +81,6 @@ struct Ws {
   float* invr2;    // [32]
   float* part;     // split-K partials
   float* qkv;      // [B][Nqkv]
-  float* qrot;     // [B][nq][D] rotated queries
   float* apart;    // [B][nq][nsplit][D + 2]
   float* h;        // [B][H]
   size_t bytes;
@@ -123,7 +122,6 @@ static Ws carve(const futx_dims& d, int B, int max_ctx, char* base) {
   w.invr2 = (float*)take(kMaxBatch * 4);
   w.part = (float*)take(part_floats(d, B) * 4);
   w.qkv = (float*)take((size_t)B * nqkv * 4);
-  w.qrot = (float*)take((size_t)B * nq * D * 4);
   w.apart = (float*)take((size_t)B * nq * (nsplit < 1 ? 1 : nsplit) * (D + 2) * 4);
   w.h = (float*)take((size_t)B * d.hidden * 4);
   w.bytes = at;
@@ -282,7 +280,6 @@ static futx_status decode_block_impl(const futx_dims* dims, const futx_block_wei
   const int B = batch, H = d.hidden, D = d.head_dim, nq = d.n_heads, G = d.w_group;
   const int nqkv = (d.n_heads + 2 * d.n_kv_heads) * D, I = d.intermediate;
   const KVPtrs kv = kv_ptrs(cache, d.n_kv_heads);
-  const KVPtrsConst kvc = kv_cptrs(cache, d.n_kv_heads);
   const size_t term = (size_t)kMaxBatch * kmax(d);
   hipError_t e;
   auto run = [stage](int k) { return stage < 0 || stage == k; };
@@ -331,17 +328,20 @@ static futx_status decode_block_impl(const futx_dims* dims, const futx_block_wei
   };
   // RMSNorm-1 + QKV (the gain is folded into the weights; 1/r in the epilogue)
   if (run(FUTX_STAGE_QKV)) STEP(gemm(w->qkv, nqkv, H, x, 1, true, kEpiRms, nullptr, ws.qkv, nullptr));
-  // RoPE, rotation, INT4 append of the new token; rotated fp32 queries
-  if (run(FUTX_STAGE_ROTATE_APPEND))
-    STEP(launch_post_qkv(ws.qkv, B, nq, D, cached_lens, block_table, max_pages_per_seq, d.had_block,
-                         d.rope_theta, ws.qrot, kv, s));
-  // attention over positions 0..cached_lens[b]
-  AttnPlan ap = attn_plan(B, d.n_kv_heads, max_context);
+  // one kernel: RoPE, rotation and INT4 append of the new token, rotated
+  // queries, attention over positions 0..cached_lens[b] in splits, four
+  // splits merged per workgroup (stage ROTATE_APPEND runs inside it) ...
+  const AttnPlan ap = attn_plan(B, d.n_kv_heads, max_context);
   if (run(FUTX_STAGE_ATTENTION))
-    STEP(launch_attention(ws.qrot, true, cached_lens, 1, block_table, max_pages_per_seq, B, nq, D,
-                          ap, kvc, ws.apart, s));
+    STEP(launch_attn_decode(ws.qkv, cached_lens, block_table, max_pages_per_seq, B, nq, D, ap, d.had_block,
+                            d.rope_theta, kv, ws.apart, s));
+  // ... then the merge of the workgroup partials, inverse rotation -> the O
+  // projection operand (three bf16 terms)
+  AttnPlan apw;
+  apw.chunk = 4 * ap.chunk;
+  apw.nsplit = (ap.nsplit + 3) / 4;
   if (run(FUTX_STAGE_MERGE))
-    STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, ap, d.had_block, nullptr, ws.act, term, s));
+    STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, apw, d.had_block, nullptr, ws.act, term, s));
   // O projection + residual: h = x + O(o)
   if (run(FUTX_STAGE_O)) STEP(gemm(w->o, H, nq * D, ws.act, 3, false, kEpiResid, x, ws.h, nullptr));
   // RMSNorm-2 + gate/up + SwiGLU -> bf16 activation

@@ -28,6 +28,7 @@ struct GemmArgs {
   int kb_per_wg;         // K blocks (128 inputs) per split
   int items;             // 16-row tiles (gate/up pairs for kEpiSwiglu)
   int wgs_per_split;     // workgroups per split, each with a run of items
+  int nw;                // waves per workgroup
   float eps;             // RMSNorm epsilon
   const float* resid;    // kEpiResid
   float* out;            // kEpiPartial / kEpiRms / kEpiResid
@@ -40,7 +41,7 @@ struct GemmLds {
   size_t act, gsum, sqg, part, ss, out, scl, total;
 };
 __host__ __device__ inline GemmLds gemm_lds_layout(int nterms, int B, int krange, int G, int ntw, int nfr,
-                                                   int items_wg, int nkb8) {
+                                                   int items_wg, int nkb8, int nw) {
   auto up = [](size_t x) { return (x + 15) & ~(size_t)15; };
   const int ngr = krange * 128 / G;
   GemmLds l;
@@ -48,7 +49,7 @@ __host__ __device__ inline GemmLds gemm_lds_layout(int nterms, int B, int krange
   l.gsum = up(l.act + (size_t)nterms * B * (krange * 128 + 8) * 2);
   l.sqg = up(l.gsum + (size_t)B * ngr * 8);
   l.part = up(l.sqg + (size_t)B * ngr * 4);
-  l.ss = up(l.part + (size_t)2 * 4 * ntw * nfr * 64 * 4);
+  l.ss = up(l.part + (size_t)2 * nw * ntw * nfr * 64 * 4);
   l.out = up(l.ss + (size_t)B * 4);
   l.scl = up(l.out + (size_t)items_wg * ntw * B * 16 * 4);
   l.total = up(l.scl + (size_t)items_wg * ntw * nkb8 * 16 * (8 * 128 / G) * 2);
@@ -56,6 +57,7 @@ __host__ __device__ inline GemmLds gemm_lds_layout(int nterms, int B, int krange
 }
 
 struct GemmPlan2 {
+  int nw = 4;  // waves per workgroup (4, 8 or 12), each owning 1 / nw of the K range
   int splits = 1;
   int kb_per_wg = 1;
   int items = 1;
@@ -77,6 +79,7 @@ inline void apply_plan(GemmArgs& a, const GemmPlan2& p) {
   a.kb_per_wg = p.kb_per_wg;
   a.items = p.items;
   a.wgs_per_split = p.wgs_per_split;
+  a.nw = p.nw;
 }
 
 }  // namespace futx

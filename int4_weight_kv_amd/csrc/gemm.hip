@@ -11,7 +11,8 @@
 //
 // Work decomposition.  A workgroup owns a run of items (16-row weight
 // tiles; for the SwiGLU projection gate/up tile pairs) over one K range, and
-// each of its four waves owns a quarter of that K range for every item.  A
+// each of its NW waves (4, or 8 for long K with few items) owns 1 / NW of
+// that K range (its "quarter" below) for every item.  A
 // wave first stages its own quarter of the activation (all batch rows) in
 // LDS as bf16 matrix-core operands (an fp32 source is rounded to bf16 there,
 // which is the RMSNorm operand rounding), together with the exact (fp64) sum
@@ -22,7 +23,7 @@
 // Then the wave streams its quarter of item after item: 128-bit loads, 16
 // bytes per lane per 1 KB tile, in chunks of eight tiles (four for gate/up
 // pairs or batches above 16) with the next chunk in flight across item
-// boundaries.  At the end of an item the four quarter sums are added in LDS
+// boundaries.  At the end of an item the NW wave sums are added in LDS
 // and one wave (rotating) keeps them; the epilogue and the only global
 // stores run after the last item.
 //
@@ -34,24 +35,34 @@
 #include "device.h"
 #include "gemm.h"
 
+#ifndef FUTX_GEMM_WIDE_NW
+#define FUTX_GEMM_WIDE_NW 8  // waves per workgroup when items are few (4, 8 or 12)
+#endif
+#ifndef FUTX_GEMM_WIDE_PCT
+#define FUTX_GEMM_WIDE_PCT 100  // "few": items <= this percentage of the CU count
+#endif
+
 namespace futx {
 
 // Register budget: at most three waves per SIMD (more would make the
 // compiler spill the prologue's staging registers), three for G = 128 and a
 // batch of up to 16, otherwise two or one.
-template <int G, int NF, int NR, int NT, bool F32, int EPI, int PAIR>
-__global__ __launch_bounds__(256, (NF == 1 && G == 128) ? 2 : 1)
+template <int G, int NF, int NR, int NT, bool F32, int EPI, int PAIR, int NW>
+__global__ __launch_bounds__(64 * NW, (NF == 1 && G == 128) ? 2 : 1)
 __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
+  constexpr int NTH = 64 * NW;                       // threads per workgroup
   constexpr int NTW = PAIR ? 2 : 1;                  // weight tiles per item (gate + up)
   constexpr int CHK = (PAIR || NF == 2) ? 4 : 8;     // K blocks per chunk and wave
-  constexpr int MAXP = (!F32 && NT == 1) ? 8 : 4;    // activation passes held in registers
+  // activation passes held in registers (one L2 round trip each batch of
+  // MAXP); fp32 rows of more than 4 sequences take 8 as well
+  constexpr int MAXP = ((!F32 && NT == 1) || (F32 && NR >= 2)) ? 8 : 4;
   extern __shared__ __align__(16) uint8_t s_dyn[];
   // LDS (gemm_lds_layout): activation range [NT][B][row] bf16 | group sums
   // [B][ngr] float2 | group sums of squares [B][ngr] | partials
   // [2][4][NTW][NF][NR][64] | ss [B] | item sums [item - it0][NTW][B][16] |
   // scales
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (0..NW-1), scalar
   const int col = lane & 15, grp = lane >> 4;
   const int B = a.B;
   const int KB = a.K >> 7;
@@ -65,7 +76,7 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
   constexpr int SEG = 8 * (128 / G);  // scales per (row, 8 K blocks)
   const int KB8 = (KB + 7) >> 3;
   const int b80 = kb0 >> 3, nkb8 = ((kb1 + 7) >> 3) - b80;
-  const GemmLds L = gemm_lds_layout(NT, B, krange, G, NTW, NF * NR, it1 - it0, nkb8);
+  const GemmLds L = gemm_lds_layout(NT, B, krange, G, NTW, NF * NR, it1 - it0, nkb8, NW);
   uint16_t* const s_act = (uint16_t*)(s_dyn + L.act);
   float2* const s_gsum = (float2*)(s_dyn + L.gsum);
   float* const s_sqg = (float*)(s_dyn + L.sqg);
@@ -76,8 +87,8 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
   // memory: [item - it0][NTW][kb / 8 - kb0 / 8][row 16][SEG]
   uint16_t* const s_scl = (uint16_t*)(s_dyn + L.scl);
 
-  // this wave's quarter of the K range, in chunks of CHK K blocks
-  const int kbq = (krange + 3) / 4;
+  // this wave's share (1 / NW) of the K range, in chunks of CHK K blocks
+  const int kbq = (krange + NW - 1) / NW;
   const int q0 = min(kb0 + wq * kbq, kb1), q1 = min(q0 + kbq, kb1);
   const int cpi = (kbq + CHK - 1) / CHK;  // chunks per item (same for every wave)
   const int nchunks = (it1 - it0) * cpi;
@@ -261,10 +272,10 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
   };
 
   auto part = [&](int slot, int w, int u, int f, int r) -> float& {
-    return s_part[((((slot * 4 + w) * NTW + u) * NF + f) * NR + r) * 64 + lane];
+    return s_part[((((slot * NW + w) * NTW + u) * NF + f) * NR + r) * 64 + lane];
   };
 
-  // end of an item: add the four quarters in LDS; one wave (rotating) keeps
+  // end of an item: add the NW wave sums in LDS; one wave (rotating) keeps
   // the item's sums in LDS while the others go on streaming.  No global
   // memory access happens here: on this target stores count in vmcnt too.
   auto finish_item = [&](int item, int slot) {
@@ -276,14 +287,27 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
         for (int r = 0; r < NR; ++r) part(slot, wq, u, f, r) = acc[u][f][r];
     zero_acc();
     __syncthreads();
-    if (wq != ((item - it0) & 3)) return;
+    if (wq != (item - it0) % NW) return;
 #pragma unroll
     for (int u = 0; u < NTW; ++u)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          const float o = (part(slot, 0, u, f, r) + part(slot, 1, u, f, r)) + (part(slot, 2, u, f, r) + part(slot, 3, u, f, r));
+          // fixed pairwise order over the NW wave sums
+          float o;
+          if constexpr (NW == 4) {
+            o = (part(slot, 0, u, f, r) + part(slot, 1, u, f, r)) + (part(slot, 2, u, f, r) + part(slot, 3, u, f, r));
+          } else {
+            float v[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v[w] = part(slot, w, u, f, r);
+#pragma unroll
+            for (int h = 1; h < NW; h <<= 1)
+#pragma unroll
+              for (int w = 0; w + h < NW; w += 2 * h) v[w] += v[w + h];
+            o = v[0];
+          }
           const int tok = b_of[f][r];
           if (tok < B) s_out[(((item - it0) * NTW + u) * B + tok) * 16 + col] = o;
         }
@@ -303,9 +327,9 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
     // four named registers, not an array: the compiler cannot index them
     static_assert(MAXS == 4, "four scale pieces per thread");
     const uint4 sr0 = *scl_src(min(tid, npieces - 1));
-    const uint4 sr1 = *scl_src(min(256 + tid, npieces - 1));
-    const uint4 sr2 = *scl_src(min(512 + tid, npieces - 1));
-    const uint4 sr3 = *scl_src(min(768 + tid, npieces - 1));
+    const uint4 sr1 = *scl_src(min(NTH + tid, npieces - 1));
+    const uint4 sr2 = *scl_src(min(2 * NTH + tid, npieces - 1));
+    const uint4 sr3 = *scl_src(min(3 * NTH + tid, npieces - 1));
     // Unconditional stores at the same clamped indices: threads past the
     // last piece rewrite it with the value they loaded from it.  No branch
     // may separate these stores from their loads, since the compiler's
@@ -313,9 +337,9 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
     // every load in flight (the weights included).
     auto store_scales = [&]() {
       ((uint4*)s_scl)[min(tid, npieces - 1)] = sr0;
-      ((uint4*)s_scl)[min(256 + tid, npieces - 1)] = sr1;
-      ((uint4*)s_scl)[min(512 + tid, npieces - 1)] = sr2;
-      ((uint4*)s_scl)[min(768 + tid, npieces - 1)] = sr3;
+      ((uint4*)s_scl)[min(NTH + tid, npieces - 1)] = sr1;
+      ((uint4*)s_scl)[min(2 * NTH + tid, npieces - 1)] = sr2;
+      ((uint4*)s_scl)[min(3 * NTH + tid, npieces - 1)] = sr3;
     };
     if (npass <= MAXP) {
       // passes past npass repeat a valid one and are skipped; the mask is
@@ -346,9 +370,21 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
       if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
     }
     // pieces beyond the registers (the planner avoids this; correct but slow)
-    for (int q = MAXS * 256 + tid; q < npieces; q += 256) ((uint4*)s_scl)[q] = *scl_src(q);
+    for (int q = MAXS * NTH + tid; q < npieces; q += NTH) ((uint4*)s_scl)[q] = *scl_src(q);
     zero_acc();
-    __syncthreads();  // scales of the whole workgroup
+    __syncthreads();  // scales (and group sums of squares) of the whole workgroup
+    // RMSNorm sums of squares of the rows, by wave 0 while the weights
+    // stream (fixed butterfly order); read after the epilogue's barrier
+    if constexpr (F32) {
+      if (wq == 0) {
+        for (int b = 0; b < B; ++b) {
+          float t = 0.f;
+          for (int g = lane; g < ngr; g += 64) t += s_sqg[(size_t)b * ngr + g];
+          t = wave_sum(t);
+          if (lane == 0) s_ss[b] = t;
+        }
+      }
+    }
   };
 
   if (nchunks == 1) {
@@ -381,16 +417,8 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
   __syncthreads();
 
   // ---- epilogue and write-out of the workgroup's items
-  if constexpr (F32) {
-    if (tid < B) {  // RMSNorm sum of squares, fixed order
-      float t = 0.f;
-      for (int g = 0; g < ngr; ++g) t += s_sqg[(size_t)tid * ngr + g];
-      s_ss[tid] = t;
-    }
-    __syncthreads();
-  }
   const int nout = (it1 - it0) * B * 16;
-  for (int idx = tid; idx < nout; idx += 256) {
+  for (int idx = tid; idx < nout; idx += NTH) {
     const int il = idx / (B * 16), rem = idx - il * B * 16, tok = rem >> 4, cc = rem & 15;
     const int n = (it0 + il) * 16 + cc;  // physical row (non-pair) / logical column (pair)
     const float o = s_out[((il * NTW) * B + tok) * 16 + cc];
@@ -427,7 +455,7 @@ size_t gemm_lds_bytes(const GemmArgs& a, int nterms, int G, bool pair) {
   const int nr = a.B <= 4 ? 1 : a.B <= 8 ? 2 : 4;
   const int items_wg = (a.items + a.wgs_per_split - 1) / a.wgs_per_split;
   const int nkb8 = (krange + 7) / 8 + 1;  // a K range not aligned to 8 blocks spans one more
-  return gemm_lds_layout(nterms, a.B, krange, G, pair ? 2 : 1, nf * nr, items_wg, nkb8).total;
+  return gemm_lds_layout(nterms, a.B, krange, G, pair ? 2 : 1, nf * nr, items_wg, nkb8, a.nw).total;
 }
 
 static size_t plan_lds(const GemmPlan2& p, int B, int G, int nterms, bool pair) {
@@ -436,6 +464,7 @@ static size_t plan_lds(const GemmPlan2& p, int B, int G, int nterms, bool pair) 
   a.kb_per_wg = p.kb_per_wg;
   a.items = p.items;
   a.wgs_per_split = p.wgs_per_split;
+  a.nw = p.nw;
   return gemm_lds_bytes(a, nterms, G, pair);
 }
 
@@ -457,15 +486,21 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   // allows three 4-wave workgroups per CU); items are spread evenly, and a
   // workgroup's item sums must fit LDS
   const int cus = device_cu_count();
+  // Waves per workgroup: when there are no more items than CUs and K is
+  // long, one workgroup per item leaves each CU with few loads in flight, so
+  // the item's K range is shared by more waves (measured on MI355X: faster
+  // for the 8B down projection, K = 14336; slower for K = 4096).
+  p.nw = 4;
+  if (p.splits == 1 && (long)items * 100 <= (long)cus * FUTX_GEMM_WIDE_PCT && KB >= 64) p.nw = FUTX_GEMM_WIDE_NW;
   const int target = (3 * cus + p.splits - 1) / p.splits;
   int per = (items + target - 1) / target;
   if (per < 1) per = 1;
-  // scale staging: at most 1024 16-byte pieces per workgroup (registers)
+  // scale staging: at most 4 16-byte pieces per thread (registers)
   const int nkb8 = (p.kb_per_wg + 7) / 8 + 1;
   auto pieces = [&](int ipw) { return (long)ipw * (pair ? 2 : 1) * nkb8 * 16 * (128 / G); };
   for (;;) {
     p.wgs_per_split = (items + per - 1) / per;
-    if (per == 1 || (plan_lds(p, B, G, nterms, pair) <= (size_t)kLdsMax && pieces(per) <= 1024)) break;
+    if (per == 1 || (plan_lds(p, B, G, nterms, pair) <= (size_t)kLdsMax && pieces(per) <= 4L * 64 * p.nw)) break;
     --per;
   }
   return p;
@@ -478,13 +513,15 @@ bool gemm_fits(int N, int K, int G, int B, int nterms, int epi) {
 
 hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi, hipStream_t st) {
   const bool pair = epi == kEpiSwiglu;
-  const dim3 grid(a.splits * a.wgs_per_split), block(256);
+  const dim3 grid(a.splits * a.wgs_per_split), block(64 * a.nw);
   if (a.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
+  if (a.nw != 4 && a.nw != FUTX_GEMM_WIDE_NW) return hipErrorInvalidValue;
   const size_t lds = gemm_lds_bytes(a, nterms, G, pair);
   if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
 #define FUTX_G(GG, NF, NR, NT, F32, EPI, PR) \
   do {                                   \
-    auto k_ = int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR>; \
+    auto k_ = a.nw == 4 ? int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR, 4> \
+                        : int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR, FUTX_GEMM_WIDE_NW>; \
     if (lds > 64 * 1024) {                                                  \
       const hipError_t e_ = hipFuncSetAttribute((const void*)k_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e_ != hipSuccess) return e_;                                      \

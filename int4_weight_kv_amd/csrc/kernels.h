@@ -39,9 +39,14 @@ hipError_t launch_swiglu(const float* part, int S, int B, int I, int G, const fl
 hipError_t launch_kv_append(const float* k, const float* v, const int32_t* positions,
                             const int32_t* slots, int n, uint32_t flags, int D, int hb,
                             float theta, const KVPtrs& kv, hipStream_t st);
-hipError_t launch_post_qkv(const float* qkv, int B, int nq, int D, const int32_t* cached_lens,
-                           const int32_t* block_table, int mpps, int hb, float theta, float* qrot,
-                           const KVPtrs& kv, hipStream_t st);
+// The attention part of the decode block before the merge (new-token
+// append, rotated queries, split attention, four splits merged per
+// workgroup): reads the QKV projection qkv [B][(nq + 2 nkv) D] fp32, writes
+// wpart [B][nq][ceil(nsplit / 4)][D + 2]; finish with launch_attn_merge
+// on a plan of 4 * chunk tokens and ceil(nsplit / 4) splits.
+hipError_t launch_attn_decode(const float* qkv, const int32_t* cached_lens, const int32_t* block_table,
+                              int mpps, int B, int nq, int D, const AttnPlan& plan, int hb, float theta,
+                              const KVPtrs& kv, float* wpart, hipStream_t st);
 // q: rotated queries [B][nq][D], fp32 (q_f32) or bf16
 hipError_t launch_attention(const void* q, bool q_f32, const int32_t* lens, int len_add,
                             const int32_t* block_table, int mpps, int B, int nq, int D,

@@ -245,43 +245,6 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const float* __restrict__
   store_token<D>(kx, vx, slots[t], h, kv);
 }
 
-// After the QKV projection: RoPE + rotation of the queries (fp32 q_rot), and
-// RoPE + rotation + INT4 append of the new key and value.
-template <int D>
-__global__ __launch_bounds__(64) void post_qkv_kernel(const float* __restrict__ qkv, int nq,
-                                                      const int32_t* __restrict__ cached_lens,
-                                                      const int32_t* __restrict__ block_table,
-                                                      int mpps, int hb, float theta,
-                                                      float* __restrict__ qrot, KVPtrs kv) {
-  const int hh = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int nkv = kv.nkv;
-  const int nqkv = (nq + 2 * nkv) * D;
-  const int pos = cached_lens[b];
-  const float* row = qkv + (size_t)b * nqkv;
-  if (hh < nq) {
-    float x[D / 64];
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) x[j] = row[hh * D + lane + 64 * j];
-    rope_lane<D>(x, pos, theta);
-    fwht_lane<D>(x, hb);
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) qrot[((size_t)b * nq + hh) * D + lane + 64 * j] = x[j];
-  } else {
-    const int h = hh - nq;
-    float kx[D / 64], vx[D / 64];
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-      kx[j] = row[(nq + h) * D + lane + 64 * j];
-      vx[j] = row[(nq + nkv + h) * D + lane + 64 * j];
-    }
-    rope_lane<D>(kx, pos, theta);
-    fwht_lane<D>(kx, hb);
-    fwht_lane<D>(vx, hb);
-    const int slot = block_table[(size_t)b * mpps + pos / kPageSize] * kPageSize + pos % kPageSize;
-    store_token<D>(kx, vx, slot, h, kv);
-  }
-}
-
 // ---------------------------------------------------------------- attention
 
 // Split-sequence decode attention.  One wave per (chunk, KV head, sequence)
@@ -318,72 +281,48 @@ __device__ __forceinline__ int range_exp(float m, int top) {
   return top - e;
 }
 
-template <int D, bool QF32>
-__global__ __launch_bounds__(64) void attn_split_kernel(
-    const void* __restrict__ qin, const int32_t* __restrict__ lens, int len_add,
-    const int32_t* __restrict__ block_table, int mpps, int nq, int chunk, int nsplit, float scale,
-    KVPtrsConst kv, float* __restrict__ apart) {
-  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const int nkv = kv.nkv, G = nq / nkv;
-  const int L = lens[b] + len_add;
-  const int t0 = sp * chunk, t1 = min(t0 + chunk, L);
-  if (t0 >= t1) return;
-  const int col = lane & 15, grp = lane >> 4;
-  // query fragments (B operand): column = query head h*G + col
-  f16x8 qh[D / 32], ql[D / 32];
-  float qscale;  // 2^-kq of this lane's head
-  {
-    const bool ok = col < G;
-    const size_t qoff = ((size_t)b * nq + h * G + col) * D;
-    float qv[D / 32][8];
-    float qmax = 0.f;
+// Query fragments (B operand of q.k): lane (col, grp) holds query head col
+// of the KV head's group, channels s * 32 + grp * 8 + e in qv[s][e] (fp32).
+// Each head is scaled by an exact power of two into fp16 range and split
+// into hi + lo fp16 operands; returns the inverse scale 2^-kq.
+template <int D>
+__device__ __forceinline__ float q_fragments(const float (&qv)[D / 32][8], f16x8 (&qh)[D / 32],
+                                             f16x8 (&ql)[D / 32]) {
+  float qmax = 0.f;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
+  for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[s][e] = 0.f;
-      if (ok) {
-        if constexpr (QF32) {
-          const float4* qp = (const float4*)((const float*)qin + qoff + s * 32 + grp * 8);
-          const float4 a = qp[0], c = qp[1];
-          qv[s][0] = a.x; qv[s][1] = a.y; qv[s][2] = a.z; qv[s][3] = a.w;
-          qv[s][4] = c.x; qv[s][5] = c.y; qv[s][6] = c.z; qv[s][7] = c.w;
-        } else {
-          const uint4 v = *(const uint4*)((const uint16_t*)qin + qoff + s * 32 + grp * 8);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qv[s][e]));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+  const int kq = range_exp(qmax, 11);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qv[s][2 * e] = bf16_bits_to_f32(w[e] & 0xFFFF);
-            qv[s][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
-          }
-        }
-      }
+  for (int s = 0; s < D / 32; ++s) {
+    uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qv[s][e]));
+    for (int e = 0; e < 8; e += 2) {
+      _Float16 h0, l0, h1, l1;
+      split_f16(ldexpf(qv[s][e], kq), &h0, &l0);
+      split_f16(ldexpf(qv[s][e + 1], kq), &h1, &l1);
+      hw[e / 2] = pack_h2(h0, h1);
+      lw[e / 2] = pack_h2(l0, l1);
     }
-    qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
-    qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
-    const int kq = range_exp(qmax, 11);
-    qscale = ldexpf(1.0f, -kq);
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        _Float16 h0, l0, h1, l1;
-        split_f16(ldexpf(qv[s][e], kq), &h0, &l0);
-        split_f16(ldexpf(qv[s][e + 1], kq), &h1, &l1);
-        hw[e / 2] = pack_h2(h0, h1);
-        lw[e / 2] = pack_h2(l0, l1);
-      }
-      qh[s] = __builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-      ql[s] = __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
-    }
+    qh[s] = __builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+    ql[s] = __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
   }
-  const float zscale = qscale * scale;
-  float m_i = -INFINITY, l_part = 0.f;
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  return ldexpf(1.0f, -kq);
+}
+
+// Online-softmax scan of tokens [t0, t1) of one sequence (block table row
+// bt) against KV head h, for the query heads of the fragments: running max
+// m_i and normalizer part l_part of head col (per lane), and the p.v
+// accumulators acc (row 4 grp + r = head, column = channel).
+template <int D>
+__device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x8 (&ql)[D / 32], float zscale,
+                                           const int32_t* bt, int t0, int t1, int h, const KVPtrsConst& kv,
+                                           float& m_i, float& l_part, f32x4 (&acc)[D / 16]) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  const int nkv = kv.nkv;
   const size_t head_bytes = (size_t)kPageSize * D / 2;
   // One 64-token page per iteration: the codes and scales of its two
   // 32-token blocks are loaded together, and the next page's table entry one
@@ -491,7 +430,6 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
         for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
       }
   };
-  const int* const bt = block_table + (size_t)b * mpps;
   int page = bt[t0 / kPageSize];
   for (int pt = t0; pt < t1; pt += kPageSize) {
     const int page_next = bt[min(pt + kPageSize, t1 - 1) / kPageSize];
@@ -503,6 +441,54 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
     if (two) compute_blk(pt + 32, r1);
     page = page_next;
   }
+}
+
+template <int D, bool QF32>
+__global__ __launch_bounds__(64) void attn_split_kernel(
+    const void* __restrict__ qin, const int32_t* __restrict__ lens, int len_add,
+    const int32_t* __restrict__ block_table, int mpps, int nq, int chunk, int nsplit, float scale,
+    KVPtrsConst kv, float* __restrict__ apart) {
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int nkv = kv.nkv, G = nq / nkv;
+  const int L = lens[b] + len_add;
+  const int t0 = sp * chunk, t1 = min(t0 + chunk, L);
+  if (t0 >= t1) return;
+  const int col = lane & 15, grp = lane >> 4;
+  // query fragments (B operand): column = query head h*G + col
+  f16x8 qh[D / 32], ql[D / 32];
+  float qscale;  // 2^-kq of this lane's head
+  {
+    const bool ok = col < G;
+    const size_t qoff = ((size_t)b * nq + h * G + col) * D;
+    float qv[D / 32][8];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[s][e] = 0.f;
+      if (ok) {
+        if constexpr (QF32) {
+          const float4* qp = (const float4*)((const float*)qin + qoff + s * 32 + grp * 8);
+          const float4 a = qp[0], c = qp[1];
+          qv[s][0] = a.x; qv[s][1] = a.y; qv[s][2] = a.z; qv[s][3] = a.w;
+          qv[s][4] = c.x; qv[s][5] = c.y; qv[s][6] = c.z; qv[s][7] = c.w;
+        } else {
+          const uint4 v = *(const uint4*)((const uint16_t*)qin + qoff + s * 32 + grp * 8);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qv[s][2 * e] = bf16_bits_to_f32(w[e] & 0xFFFF);
+            qv[s][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
+          }
+        }
+      }
+    }
+    qscale = q_fragments<D>(qv, qh, ql);
+  }
+  float m_i = -INFINITY, l_part = 0.f;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  split_scan<D>(qh, ql, qscale * scale, block_table + (size_t)b * mpps, t0, t1, h, kv, m_i, l_part, acc);
   // finalize this chunk's partials
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
@@ -523,6 +509,202 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
           const int c = cg * 64 + c4 * 16 + col;
           out[i * head_stride + 2 + c] = acc[cg * 4 + c4][r];
         }
+    }
+  }
+}
+
+// One butterfly step (distance HOP channels) of the block Hadamard on query
+// values held as channel s * 32 + grp * 8 + e in qv[s][e] (lane = grp * 16 +
+// col): the same pairing and formula as fwht_lane.
+template <int D, int HOP>
+__device__ __forceinline__ void q_hop(float (&qv)[D / 32][8], int lane) {
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (HOP < 8) {
+        if (!(e & HOP)) {
+          const float x0 = qv[s][e], x1 = qv[s][e + HOP];
+          qv[s][e] = x0 + x1;
+          qv[s][e + HOP] = x0 - x1;
+        }
+      } else if constexpr (HOP < 32) {
+        constexpr int LB = HOP == 8 ? 16 : 32;
+        const float o = __shfl_xor(qv[s][e], LB, 64);
+        qv[s][e] = (lane & LB) ? o - qv[s][e] : qv[s][e] + o;
+      } else if constexpr (D / 32 > 1) {
+        if (!(s & 1)) {
+          const float x0 = qv[s][e], x1 = qv[s + 1][e];
+          qv[s][e] = x0 + x1;
+          qv[s + 1][e] = x0 - x1;
+        }
+      }
+    }
+}
+
+// o (fp32, channel c of query head i) -> the O projection operand: three
+// bf16 terms hi + mid + lo (24 significant bits), term t at out + t * stride.
+__device__ __forceinline__ void store_three_terms(float o, uint16_t* out, size_t at, size_t term_stride) {
+  const uint16_t t0 = f32_to_bf16_bits(o);
+  const float r1 = o - bf16_bits_to_f32(t0);
+  const uint16_t t1 = f32_to_bf16_bits(r1);
+  const uint16_t t2 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(t1));
+  out[at] = t0;
+  out[at + term_stride] = t1;
+  out[at + 2 * term_stride] = t2;
+}
+
+// The attention part of the decode block after the QKV projection, up to
+// the cross-workgroup merge (attn_merge_kernel, with 4 * chunk tokens per
+// partial):
+//   * the new token: RoPE of k at position L_b, block rotation of k and v,
+//     per-token INT4 quantization, write to the paged cache at slot L_b;
+//   * the rotated queries (RoPE + block rotation) of the G query heads of
+//     the KV head, recomputed by every wave from the fp32 projection;
+//   * split-sequence attention over positions 0..L_b (the new token read
+//     back from the cache), four splits per workgroup (one per wave),
+//     merged in LDS into one partial (m, l, acc) per workgroup and head.
+// Steps from the FuTransformer pages: K/V rotated by a block Hadamard before
+// INT4 caching and the rotation undone on the output (kongchang.com/en,
+// section "INT4 Decode: letting dequantization feed directly into MMA
+// operands"); results written straight into cache locations (same article,
+// section "FP8 Prefill: fusing GEMM and epilogue all the way").
+// wpart[((b * nq + i) * nwg + w) * (D + 2)] = {m, l, acc[0..D)} of workgroup w.
+// (A merge in this kernel by the last workgroup to finish needs device-scope
+// fences around a counter; on this chip each one writes back the L2, and
+// that cost more than the separate merge launch.)
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_kernel(
+    const float* __restrict__ qkv, int nq, const int32_t* __restrict__ cached_lens,
+    const int32_t* __restrict__ block_table, int mpps, int chunk, int nwg, int hb, float theta, float scale,
+    KVPtrs kv, float* __restrict__ wpart) {
+  constexpr int MAXG = 16;  // query heads per KV head (matrix-core columns)
+  __shared__ float s_m[4][MAXG], s_l[4][MAXG];
+  __shared__ float s_acc[4][MAXG][D];
+  const int wg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nkv = kv.nkv, G = nq / nkv;
+  const int pos = cached_lens[b];  // the new token's position
+  const int T = pos + 1;           // tokens attended to
+  const int nsp = (T + chunk - 1) / chunk;
+  const int nwg_b = (nsp + 3) / 4;
+  if (wg >= nwg_b) return;  // the whole workgroup, before any barrier
+  const float* row = qkv + (size_t)b * (nq + 2 * nkv) * D;
+  const KVPtrsConst kvc{kv.k_codes, kv.v_codes, kv.k_scales, kv.v_scales, nkv};
+
+  // 1. the new token's key and value, by the wave of the last split (the
+  //    only wave that reads the token's page), before its scan
+  if (wg * 4 + wv == nsp - 1) {
+    float kx[D / 64], vx[D / 64];
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      kx[j] = row[(nq + h) * D + lane + 64 * j];
+      vx[j] = row[(nq + nkv + h) * D + lane + 64 * j];
+    }
+    rope_lane<D>(kx, pos, theta);
+    fwht_lane<D>(kx, hb);
+    fwht_lane<D>(vx, hb);
+    const int slot = block_table[(size_t)b * mpps + pos / kPageSize] * kPageSize + pos % kPageSize;
+    store_token<D>(kx, vx, slot, h, kv);
+    // The scan below reads the token back; only this wave reads its page.
+    // One wave's memory operations reach the (write-through) L1 and the L2
+    // in program order, so its later loads see these stores and atomics; the
+    // workgroup-scope fence only keeps the compiler from reordering them.
+    // (A device-scope fence would write back the whole L2, which costs
+    // microseconds per call on this chip.)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  }
+
+  // 2. rotated queries of the group's heads, as matrix-core fragments
+  f16x8 qh[D / 32], ql[D / 32];
+  float qscale;
+  {
+    float cs, sn;  // cos / sin of frequency index lane % (D / 2)
+    rope_cs(pos, lane % (D / 2), D, theta, &cs, &sn);
+    const bool ok = col < G;
+    const float* qrow = row + (size_t)(h * G + (ok ? col : 0)) * D;
+    float qv[D / 32][8];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const float4* qp = (const float4*)(qrow + s * 32 + grp * 8);
+      const float4 a = qp[0], c = qp[1];
+      qv[s][0] = a.x; qv[s][1] = a.y; qv[s][2] = a.z; qv[s][3] = a.w;
+      qv[s][4] = c.x; qv[s][5] = c.y; qv[s][6] = c.z; qv[s][7] = c.w;
+    }
+    // rotate-half RoPE: channel c < D/2 (word s) pairs with c + D/2 (word s + D/64)
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int fi = s * 32 + grp * 8 + e;
+        const float c = __shfl(cs, fi, 64), sv = __shfl(sn, fi, 64);
+        const float x0 = qv[s][e], x1 = qv[s + D / 64][e];
+        qv[s][e] = x0 * c - x1 * sv;
+        qv[s + D / 64][e] = x1 * c + x0 * sv;
+      }
+    // block Hadamard over channel bits: 0..2 in e, 3..4 in grp (lanes 16
+    // and 32 apart), 5 in the word index s; one call per hop, so every
+    // register index is a compile-time constant
+    if (hb > 1) q_hop<D, 1>(qv, lane);
+    if (hb > 2) q_hop<D, 2>(qv, lane);
+    if (hb > 4) q_hop<D, 4>(qv, lane);
+    if (hb > 8) q_hop<D, 8>(qv, lane);
+    if (hb > 16) q_hop<D, 16>(qv, lane);
+    if (hb > 32) q_hop<D, 32>(qv, lane);
+    const float hsc = 1.0f / sqrtf((float)hb);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[s][e] = ok ? qv[s][e] * hsc : 0.f;
+    qscale = q_fragments<D>(qv, qh, ql);
+  }
+
+  // 3. this wave's split
+  const int t0 = (wg * 4 + wv) * chunk, t1 = min(t0 + chunk, T);
+  float m_i = -INFINITY, l_part = 0.f;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (t0 < t1)
+    split_scan<D>(qh, ql, qscale * scale, block_table + (size_t)b * mpps, t0, t1, h, kvc, m_i, l_part, acc);
+  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+
+  // 4. the four splits of the workgroup, merged in LDS
+  if (grp == 0 && col < G) {
+    s_m[wv][col] = m_i;
+    s_l[wv][col] = l_tot;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * grp + r;
+    if (i < G) {
+#pragma unroll
+      for (int cg = 0; cg < D / 64; ++cg)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) s_acc[wv][i][cg * 64 + c4 * 16 + col] = acc[cg * 4 + c4][r];
+    }
+  }
+  __syncthreads();
+  const size_t hstride = (size_t)nwg * (D + 2);  // between query heads in wpart
+  float* wp = wpart + (((size_t)b * nq + h * G) * nwg + wg) * (D + 2);
+  for (int p = tid; p < G * D; p += 256) {
+    const int i = p / D, c = p % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][i]);
+    float l = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // a wave with no tokens has m = -inf: weight 0
+      const float wt = s_m[w][i] == -INFINITY ? 0.f : expf(s_m[w][i] - M);
+      l = fmaf(wt, s_l[w][i], l);
+      a = fmaf(wt, s_acc[w][i][c], a);
+    }
+    wp[i * hstride + 2 + c] = a;
+    if (c == 0) {
+      wp[i * hstride] = M;
+      wp[i * hstride + 1] = l;
     }
   }
 }
@@ -609,16 +791,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   }
   o *= 1.0f / sqrtf((float)hb);
   if (out_f32) out_f32[((size_t)b * nq + i) * D + c] = o;
-  if (out_bf16) {  // o as three bf16 terms (hi + mid + lo), the O projection operand
-    const uint16_t t0 = f32_to_bf16_bits(o);
-    const float r1 = o - bf16_bits_to_f32(t0);
-    const uint16_t t1 = f32_to_bf16_bits(r1);
-    const uint16_t t2 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(t1));
-    const size_t at = (size_t)b * nq * D + (size_t)i * D + c;
-    out_bf16[at] = t0;
-    out_bf16[at + term_stride] = t1;
-    out_bf16[at + 2 * term_stride] = t2;
-  }
+  if (out_bf16)  // o as three bf16 terms (hi + mid + lo), the O projection operand
+    store_three_terms(o, out_bf16, (size_t)b * nq * D + (size_t)i * D + c, term_stride);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -669,14 +843,19 @@ hipError_t launch_kv_append(const float* k, const float* v, const int32_t* posit
   return hipSuccess;
 }
 
-hipError_t launch_post_qkv(const float* qkv, int B, int nq, int D, const int32_t* cached_lens,
-                           const int32_t* block_table, int mpps, int hb, float theta, float* qrot,
-                           const KVPtrs& kv, hipStream_t st) {
-  const dim3 grid(nq + kv.nkv, B);
+hipError_t launch_attn_decode(const float* qkv, const int32_t* cached_lens, const int32_t* block_table,
+                              int mpps, int B, int nq, int D, const AttnPlan& plan, int hb, float theta,
+                              const KVPtrs& kv, float* wpart, hipStream_t st) {
+  if (nq % kv.nkv != 0 || nq / kv.nkv > 16) return hipErrorInvalidValue;
+  const int nwg = (plan.nsplit + 3) / 4;
+  const dim3 grid(nwg, kv.nkv, B);
+  const float scale = 1.0f / sqrtf((float)D);
   if (D == 128)
-    post_qkv_kernel<128><<<grid, 64, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, hb, theta, qrot, kv);
+    attn_decode_kernel<128><<<grid, 256, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, plan.chunk, nwg, hb,
+                                                   theta, scale, kv, wpart);
   else
-    post_qkv_kernel<64><<<grid, 64, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, hb, theta, qrot, kv);
+    attn_decode_kernel<64><<<grid, 256, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, plan.chunk, nwg, hb,
+                                                  theta, scale, kv, wpart);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }

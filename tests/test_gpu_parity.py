@@ -128,6 +128,39 @@ def test_kv_append_full_chain(F, DB, shape):
     say("boundary flips (codes, scales): keys", fk, "values", fv)
 
 
+def test_kv_append_rotation_ablation(F, DB):
+    """The device cache written with and without the block rotation on the
+    outlier-key workload: each flag setting matches the oracle's chain, and
+    the rotation cuts the key error (the pages' claim; the oracle-only
+    version is in test_rotation_ablation.py)."""
+    wl = W.llama8b_ragged(1)
+    d = wl.dims
+    n, num_pages = 512, 8
+    k, v = W.history(wl, 0, 0, n)
+    pos = np.arange(n, dtype=np.int32)
+    k_rope = oracle.rope_rotate_half(k.astype(np.float64), pos[:, None], d.rope_theta)
+    v64 = v.astype(np.float64)
+    errs = {}
+    for rot in (False, True):
+        flags = F.FUTX_KV_ROPE | (F.FUTX_KV_HADAMARD if rot else 0)
+        cache = DB.DeviceKVCache(d, num_pages)
+        say("kv_append ablation, rotation", rot)
+        cache.append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(pos).cuda(),
+                     torch.from_numpy(pos.copy()).cuda(), flags=flags)
+        torch.cuda.synchronize()
+        K, KS, V, VS = _cache_tokens(cache.host_copy(), d, num_pages, pos)
+        kx = oracle.block_diag_rotate(k_rope, d.had_block) if rot else k_rope
+        vx = oracle.block_diag_rotate(v64, d.had_block) if rot else v64
+        _flip_tolerant(K, KS, kx, "keys")
+        _flip_tolerant(V, VS, vx, "values")
+        kh = K.astype(np.float64) * KS.astype(np.float64)[..., None]
+        if rot:
+            kh = oracle.block_diag_rotate(kh, d.had_block)
+        errs[rot] = float(np.linalg.norm(kh - k_rope) / np.linalg.norm(k_rope))
+    say("relative key error without / with rotation", errs[False], errs[True])
+    assert errs[True] < 0.5 * errs[False], errs
+
+
 # ---------------------------------------------------------------- projections
 
 
