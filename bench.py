@@ -259,7 +259,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="8b-b1")
     ap.add_argument("--layers", type=int, default=0, help="layer instances cycled (default: enough to exceed MALL)")
-    ap.add_argument("--phase", default="all", choices=["all", "block", "dominant", "copy"])
+    ap.add_argument("--phase", default="all", choices=["all", "block", "dominant", "copy", "stages"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
@@ -381,6 +381,29 @@ def main():
                 "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
             },
         })
+
+    if args.phase == "stages":
+        # per-stage times (futx_decode_block_stage), each stage replayed alone
+        # from a graph over the cycled layers; stage 1 runs inside stage 2
+        names = ["qkv", "rotate_append", "attention", "merge", "o", "gateup", "down"]
+        res = {"phase": "stages", "workload": args.workload, "batch": int(wl.batch), "layers": nl, "unit": "us"}
+        g_blk = capture(block, 4 * nl)
+        ms, n = timed([(g_blk, 4 * nl)], max(1, args.steps // (4 * nl)))
+        res["block"] = round(ms * 1e3 / n, 2)
+        for si, nm in enumerate(names):
+            if nm == "rotate_append":
+                continue
+            fn = lambda i, si=si: runner.stage(layers[i % nl], caches[i % nl], x, si)
+            g = capture(fn, 4 * nl)
+            with torch.cuda.stream(stream):
+                g.replay()
+            stream.synchronize()
+            ms, n = timed([(g, 4 * nl)], max(1, args.steps // (4 * nl)))
+            res[nm] = round(ms * 1e3 / n, 2)
+        res["algorithmic_bytes"] = int(step_bytes)
+        res["block_GBps"] = round(step_bytes / (res["block"] * 1e-6) / 1e9, 1)
+        print(json.dumps(res), flush=True)
+        return
 
     if args.phase in ("all", "dominant"):
         # the dominant kernel alone: gate/up + SwiGLU stage, cycling layers

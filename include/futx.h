@@ -149,6 +149,25 @@ futx_status futx_pack_weights(const futx_dims* dims, futx_proj proj, const float
 futx_status futx_pack_weights_host(const futx_dims* dims, futx_proj proj, const float* w_host,
                                    const float* gain_host, void* packed_host, void* scales_host);
 
+/* Ingestion of codes quantized elsewhere in the same format (the pages name
+ * GPTQ weights "in the same format" as the alternative to round-to-nearest
+ * [ACC]): canonical bytes [N][K/2] (byte i of a row = code 2i in the low
+ * nibble, code 2i+1 in the high nibble, two's complement, every code in
+ * [-8, 7] accepted) and fp16 scales [N][K/w_group] in logical row order
+ * (host), reordered into the device order of futx_pack_weights.  No folding
+ * or quantization happens: a gain must already be in the codes and scales.
+ * FUTX_E_RANGE if a scale is not a finite fp16 value.  Returns after the
+ * copies have completed. */
+futx_status futx_pack_codes(const futx_dims* dims, futx_proj proj, const uint8_t* codes_host,
+                            const uint16_t* scales_host, void* packed_dev, void* scales_dev,
+                            void* stream);
+
+/* Same as futx_pack_codes but writes the device-order bytes to host buffers
+ * (no HIP call). */
+futx_status futx_pack_codes_host(const futx_dims* dims, futx_proj proj, const uint8_t* codes_host,
+                                 const uint16_t* scales_host, void* packed_host,
+                                 void* packed_scales_host);
+
 /* Inverse of the device order (for tests): reads packed_dev / scales_dev and
  * writes canonical bytes [N][K/2] (byte i of a row = code 2i in the low
  * nibble, code 2i+1 in the high nibble, two's complement) and fp16 scales

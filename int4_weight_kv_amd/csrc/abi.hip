@@ -15,6 +15,8 @@ namespace futx {
 
 futx_status pack_host(const futx_dims* dims, futx_proj proj, const float* w, const float* gain,
                       void* packed, void* scales);
+futx_status pack_codes_host(const futx_dims* dims, futx_proj proj, const uint8_t* canon,
+                            const uint16_t* canon_scales, void* packed, void* scales);
 futx_status unpack_host(const futx_dims* dims, futx_proj proj, const void* packed,
                         const void* scales, uint8_t* canon, uint16_t* canon_scales);
 futx_status fold_head_host(int32_t vocab, int32_t hidden, const uint16_t* w, const float* gain,
@@ -193,6 +195,30 @@ futx_status futx_pack_weights(const futx_dims* dims, futx_proj proj, const float
   FUTX_HIP(hipMemcpyAsync(packed_dev, hp.data(), pb, hipMemcpyHostToDevice, s), "pack: copy");
   FUTX_HIP(hipMemcpyAsync(scales_dev, hs.data(), sb, hipMemcpyHostToDevice, s), "pack: copy");
   FUTX_HIP(hipStreamSynchronize(s), "pack: sync");
+  return FUTX_OK;
+}
+
+futx_status futx_pack_codes_host(const futx_dims* dims, futx_proj proj, const uint8_t* codes_host,
+                                 const uint16_t* scales_host, void* packed_host, void* packed_scales_host) {
+  clear_error();
+  return pack_codes_host(dims, proj, codes_host, scales_host, packed_host, packed_scales_host);
+}
+
+futx_status futx_pack_codes(const futx_dims* dims, futx_proj proj, const uint8_t* codes_host,
+                            const uint16_t* scales_host, void* packed_dev, void* scales_dev, void* stream) {
+  clear_error();
+  size_t pb, sb;
+  futx_status st = futx_packed_sizes(dims, proj, &pb, &sb);
+  if (st) return st;
+  if (!packed_dev || !scales_dev) return fail(FUTX_E_ARG, "pack_codes: null device pointer");
+  std::vector<uint8_t> hp(pb);
+  std::vector<uint8_t> hs(sb);
+  st = pack_codes_host(dims, proj, codes_host, scales_host, hp.data(), hs.data());
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  FUTX_HIP(hipMemcpyAsync(packed_dev, hp.data(), pb, hipMemcpyHostToDevice, s), "pack_codes: copy");
+  FUTX_HIP(hipMemcpyAsync(scales_dev, hs.data(), sb, hipMemcpyHostToDevice, s), "pack_codes: copy");
+  FUTX_HIP(hipStreamSynchronize(s), "pack_codes: sync");
   return FUTX_OK;
 }
 

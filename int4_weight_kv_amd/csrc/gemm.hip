@@ -38,6 +38,12 @@
 #ifndef FUTX_GEMM_WIDE_NW
 #define FUTX_GEMM_WIDE_NW 8  // waves per workgroup when items are few (4, 8 or 12)
 #endif
+#ifndef FUTX_GEMM_OCC
+#define FUTX_GEMM_OCC 3  // workgroups per CU the item split aims at (batch <= 4)
+#endif
+#ifndef FUTX_GEMM_OCC_BATCH
+#define FUTX_GEMM_OCC_BATCH 1  // the same for batches above 4
+#endif
 #ifndef FUTX_GEMM_WIDE_PCT
 #define FUTX_GEMM_WIDE_PCT 100  // "few": items <= this percentage of the CU count
 #endif
@@ -482,8 +488,8 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   p.kb_per_wg = (KB + p.splits - 1) / p.splits;
   p.splits = (KB + p.kb_per_wg - 1) / p.kb_per_wg;
   p.items = items;
-  // about three resident workgroups per CU in total (the register budget
-  // allows three 4-wave workgroups per CU); items are spread evenly, and a
+  // at most three resident workgroups per CU (the register budget allows
+  // three 4-wave workgroups per CU); items are spread evenly, and a
   // workgroup's item sums must fit LDS
   const int cus = device_cu_count();
   // Waves per workgroup: when there are no more items than CUs and K is
@@ -492,7 +498,12 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   // for the 8B down projection, K = 14336; slower for K = 4096).
   p.nw = 4;
   if (p.splits == 1 && (long)items * 100 <= (long)cus * FUTX_GEMM_WIDE_PCT && KB >= 64) p.nw = FUTX_GEMM_WIDE_NW;
-  const int target = (3 * cus + p.splits - 1) / p.splits;
+  // Workgroups per CU aimed at: three for up to 4 sequences; one above,
+  // where every workgroup stages B activation rows, so fewer workgroups
+  // with more items each stage less (measured on MI355X at batch 8: the 8B
+  // gate/up projection 32.1 -> 23.4 us; at batch 1 three per CU is best).
+  const int occ = B <= 4 ? FUTX_GEMM_OCC : FUTX_GEMM_OCC_BATCH;
+  const int target = (occ * cus + p.splits - 1) / p.splits;
   int per = (items + target - 1) / target;
   if (per < 1) per = 1;
   // scale staging: at most 4 16-byte pieces per thread (registers)

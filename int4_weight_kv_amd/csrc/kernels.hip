@@ -316,11 +316,14 @@ __device__ __forceinline__ float q_fragments(const float (&qv)[D / 32][8], f16x8
 // Online-softmax scan of tokens [t0, t1) of one sequence (block table row
 // bt) against KV head h, for the query heads of the fragments: running max
 // m_i and normalizer part l_part of head col (per lane), and the p.v
-// accumulators acc (row 4 grp + r = head, column = channel).
-template <int D>
-__device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x8 (&ql)[D / 32], float zscale,
-                                           const int32_t* bt, int t0, int t1, int h, const KVPtrsConst& kv,
-                                           float& m_i, float& l_part, f32x4 (&acc)[D / 16]) {
+// accumulators acc (row 4 grp + r = head, column = channel).  make_q() runs
+// once, after the first page's loads are issued and before its scores, and
+// may fill the fragments and zscale (their latency then overlaps).
+template <int D, typename MakeQ>
+__device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x8 (&ql)[D / 32],
+                                           const float& zscale, const int32_t* bt, int t0, int t1, int h,
+                                           const KVPtrsConst& kv, float& m_i, float& l_part,
+                                           f32x4 (&acc)[D / 16], MakeQ&& make_q) {
   const int lane = threadIdx.x & 63, grp = lane >> 4;
   const int nkv = kv.nkv;
   const size_t head_bytes = (size_t)kPageSize * D / 2;
@@ -431,16 +434,19 @@ __device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x
       }
   };
   int page = bt[t0 / kPageSize];
-  for (int pt = t0; pt < t1; pt += kPageSize) {
+  auto step = [&](int pt, bool first) {
     const int page_next = bt[min(pt + kPageSize, t1 - 1) / kPageSize];
     Blk r0, r1;
     load_blk(page, pt % kPageSize, r0);
     const bool two = pt + 32 < t1 && (pt % kPageSize) == 0;
     load_blk(page, two ? 32 : pt % kPageSize, r1);
+    if (first) make_q();
     compute_blk(pt, r0);
     if (two) compute_blk(pt + 32, r1);
     page = page_next;
-  }
+  };
+  step(t0, true);  // first page peeled: the query work overlaps its loads
+  for (int pt = t0 + kPageSize - t0 % kPageSize; pt < t1; pt += kPageSize) step(pt, false);
 }
 
 template <int D, bool QF32>
@@ -488,7 +494,8 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   f32x4 acc[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  split_scan<D>(qh, ql, qscale * scale, block_table + (size_t)b * mpps, t0, t1, h, kv, m_i, l_part, acc);
+  const float zscale = qscale * scale;
+  split_scan<D>(qh, ql, zscale, block_table + (size_t)b * mpps, t0, t1, h, kv, m_i, l_part, acc, [] {});
   // finalize this chunk's partials
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
@@ -617,14 +624,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 
   // 2. rotated queries of the group's heads, as matrix-core fragments
+  //    (computed inside the scan, while the first page's loads are in flight)
+  //    The query loads go out first (loads complete in order, so the KV
+  //    loads issued after them stay in flight while the queries are used).
   f16x8 qh[D / 32], ql[D / 32];
-  float qscale;
+  float zscale = 0.f;
+  const bool ok = col < G;
+  float qv[D / 32][8];
   {
-    float cs, sn;  // cos / sin of frequency index lane % (D / 2)
-    rope_cs(pos, lane % (D / 2), D, theta, &cs, &sn);
-    const bool ok = col < G;
     const float* qrow = row + (size_t)(h * G + (ok ? col : 0)) * D;
-    float qv[D / 32][8];
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       const float4* qp = (const float4*)(qrow + s * 32 + grp * 8);
@@ -632,6 +640,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       qv[s][0] = a.x; qv[s][1] = a.y; qv[s][2] = a.z; qv[s][3] = a.w;
       qv[s][4] = c.x; qv[s][5] = c.y; qv[s][6] = c.z; qv[s][7] = c.w;
     }
+  }
+  auto make_q = [&]() {
+    float cs, sn;  // cos / sin of frequency index lane % (D / 2)
+    rope_cs(pos, lane % (D / 2), D, theta, &cs, &sn);
     // rotate-half RoPE: channel c < D/2 (word s) pairs with c + D/2 (word s + D/64)
 #pragma unroll
     for (int s = 0; s < D / 64; ++s)
@@ -657,8 +669,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[s][e] = ok ? qv[s][e] * hsc : 0.f;
-    qscale = q_fragments<D>(qv, qh, ql);
-  }
+    zscale = q_fragments<D>(qv, qh, ql) * scale;
+  };
 
   // 3. this wave's split
   const int t0 = (wg * 4 + wv) * chunk, t1 = min(t0 + chunk, T);
@@ -667,7 +679,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (t0 < t1)
-    split_scan<D>(qh, ql, qscale * scale, block_table + (size_t)b * mpps, t0, t1, h, kvc, m_i, l_part, acc);
+    split_scan<D>(qh, ql, zscale, block_table + (size_t)b * mpps, t0, t1, h, kvc, m_i, l_part, acc, make_q);
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
 
@@ -860,11 +872,16 @@ hipError_t launch_attn_decode(const float* qkv, const int32_t* cached_lens, cons
   return hipSuccess;
 }
 
+#ifndef FUTX_ATTN_SPLITS
+#define FUTX_ATTN_SPLITS 2048
+#endif
+
 AttnPlan attn_plan(int B, int nkv, int max_context) {
   AttnPlan p;
   const int pages = (max_context + kPageSize - 1) / kPageSize;
   const long work = (long)B * nkv * pages;  // page-sized work items
-  int cp = (int)((work + 2047) / 2048);
+  // pages per split: at most FUTX_ATTN_SPLITS splits (waves) in total
+  int cp = (int)((work + FUTX_ATTN_SPLITS - 1) / FUTX_ATTN_SPLITS);
   cp = cp < 1 ? 1 : cp;
   p.chunk = cp * kPageSize;
   p.nsplit = (max_context + p.chunk - 1) / p.chunk;

@@ -143,6 +143,41 @@ futx_status pack_host(const futx_dims* dims, futx_proj proj, const float* w, con
   return FUTX_OK;
 }
 
+futx_status pack_codes_host(const futx_dims* dims, futx_proj proj, const uint8_t* canon,
+                            const uint16_t* canon_scales, void* packed, void* scales) {
+  futx_status st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_proj(proj))) return st;
+  if (!canon || !canon_scales || !packed || !scales) return fail(FUTX_E_ARG, "pack_codes: null pointer");
+  ProjShape ps = proj_shape(*dims, proj);
+  const int kblocks = ps.k / kTileK, ngroups = ps.k / dims->w_group;
+  for (size_t i = 0; i < (size_t)ps.n * ngroups; ++i)
+    if ((canon_scales[i] & 0x7C00u) == 0x7C00u)
+      return fail(FUTX_E_RANGE, "pack_codes: scale %zu is not a finite fp16 value", i);
+  uint8_t* pk = (uint8_t*)packed;
+  uint16_t* sc = (uint16_t*)scales;
+  std::memset(scales, 0, 2 * scale_count(ps.n, kblocks, dims->w_group));  // padding
+  for (int n = 0; n < ps.n; ++n) {
+    const int P = proj == FUTX_PROJ_GATEUP ? gateup_physical_row(n, dims->intermediate) : n;
+    for (int g = 0; g < ngroups; ++g)
+      sc[scale_index(P, g, kblocks, dims->w_group)] = canon_scales[(size_t)n * ngroups + g];
+    for (int c = 0; c < ps.k; ++c) {
+      // canonical byte: element 2i in the low nibble, 2i + 1 in the high
+      // nibble, two's-complement codes in [-8, 7]
+      const uint32_t nib = (canon[(size_t)n * (ps.k / 2) + c / 2] >> (4 * (c & 1))) & 15u;
+      const int code = (int)(nib ^ 8u) - 8;
+      size_t off;
+      int e;
+      weight_nibble_pos(P, c, kblocks, &off, &e);
+      uint32_t word;
+      std::memcpy(&word, pk + off, 4);
+      word = nibble_put(word, e, (uint32_t)(code + (int)kNibbleBias));
+      std::memcpy(pk + off, &word, 4);
+    }
+  }
+  return FUTX_OK;
+}
+
 futx_status unpack_host(const futx_dims* dims, futx_proj proj, const void* packed,
                         const void* scales, uint8_t* canon, uint16_t* canon_scales) {
   ProjShape ps = proj_shape(*dims, proj);

@@ -89,6 +89,8 @@ _SIGS = {
     "futx_packed_sizes": (_I32, [_D, _I32, _SZ, _SZ]),
     "futx_pack_weights": (_I32, [_D, _I32, _P, _P, _P, _P, _P]),
     "futx_pack_weights_host": (_I32, [_D, _I32, _P, _P, _P, _P]),
+    "futx_pack_codes": (_I32, [_D, _I32, _P, _P, _P, _P, _P]),
+    "futx_pack_codes_host": (_I32, [_D, _I32, _P, _P, _P, _P]),
     "futx_unpack_weights": (_I32, [_D, _I32, _P, _P, _P, _P, _P]),
     "futx_kv_cache_sizes": (_I32, [_D, _I32, _SZ, _SZ]),
     "futx_kv_append": (_I32, [_D, _I32, _P, _P, _P, _P, ctypes.c_uint32, ctypes.POINTER(futx_kv_cache), _P]),
@@ -180,6 +182,22 @@ def futx_pack_weights_host(dims, proj, w_host, gain_host, packed_host, scales_ho
     _check("futx_pack_weights_host", _lib.futx_pack_weights_host(ctypes.byref(make_dims(dims)), _proj(proj),
                                                                  _ptr(w_host), _ptr(g), _ptr(packed_host),
                                                                  _ptr(scales_host)))
+
+
+def futx_pack_codes(dims, proj, codes_host, scales_host, packed_dev, scales_dev, stream=None):
+    codes_host = np.ascontiguousarray(codes_host, dtype=np.uint8)
+    scales_host = np.ascontiguousarray(scales_host, dtype=np.uint16)
+    _check("futx_pack_codes", _lib.futx_pack_codes(ctypes.byref(make_dims(dims)), _proj(proj), _ptr(codes_host),
+                                                   _ptr(scales_host), _ptr(packed_dev), _ptr(scales_dev),
+                                                   _stream(stream)))
+
+
+def futx_pack_codes_host(dims, proj, codes_host, scales_host, packed_host, packed_scales_host):
+    codes_host = np.ascontiguousarray(codes_host, dtype=np.uint8)
+    scales_host = np.ascontiguousarray(scales_host, dtype=np.uint16)
+    _check("futx_pack_codes_host", _lib.futx_pack_codes_host(ctypes.byref(make_dims(dims)), _proj(proj),
+                                                             _ptr(codes_host), _ptr(scales_host),
+                                                             _ptr(packed_host), _ptr(packed_scales_host)))
 
 
 def futx_unpack_weights(dims, proj, packed_dev, scales_dev, canon_bytes_host, canon_scales_host, stream=None):

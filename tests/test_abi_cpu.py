@@ -137,6 +137,65 @@ def test_host_pack_bit_exact_tiny(fx, proj):
     np.testing.assert_array_equal(sc.view(np.uint16), want_s.view(np.uint16))
 
 
+def _host_pack_codes(fx, dims, proj, canon, canon_scales):
+    pb, sb = fx.futx_packed_sizes(dims, proj)
+    packed = np.zeros(pb, np.uint8)
+    scales = np.zeros(sb // 2, np.uint16)
+    fx.futx_pack_codes_host(dims, proj, canon, canon_scales, packed, scales)
+    return packed, scales
+
+
+@pytest.mark.parametrize("proj", ["qkv", "o", "gateup", "down"])
+def test_pack_codes_equals_rtn_pack(fx, proj):
+    """Codes and scales quantized outside the library (here: the oracle's
+    round-to-nearest) enter through futx_pack_codes_host and give exactly
+    the device bytes of futx_pack_weights_host on the same weights."""
+    wl = W.tiny()
+    w = W.block_weights(wl, 0)
+    d = wl.dims
+    mats = {"qkv": (w["wqkv"], w["gain_attn"]), "o": (w["wo"], None),
+            "gateup": (np.concatenate([w["wgate"], w["wup"]]), w["gain_ffn"]), "down": (w["wdown"], None)}
+    m, g = mats[proj]
+    folded = m if g is None else oracle.fold_gain(m, g)
+    q, s = oracle.quantize_weight_rtn(folded, d.w_group)
+    got_p, got_s = _host_pack_codes(fx, d, proj, oracle.pack_nibbles(q), s.view(np.uint16))
+    want_p, want_s = _host_pack(fx, d, proj, m, g)
+    np.testing.assert_array_equal(got_p, want_p)
+    np.testing.assert_array_equal(got_s, want_s)
+
+
+@pytest.mark.parametrize("proj", ["qkv", "gateup", "down"])
+def test_pack_codes_full_code_range(fx, proj):
+    """Every code in [-8, 7] (-8 never comes out of max/7 round-to-nearest,
+    but external quantizers may use it) and arbitrary finite scales survive
+    the reorder, read back by the independent layout decoder."""
+    d = W.TINY
+    r = np.random.default_rng(31)
+    pb, _ = fx.futx_packed_sizes(d, proj)
+    n, k = {"qkv": (512, 256), "gateup": (1536, 256), "down": (256, 768)}[proj]
+    q = r.integers(-8, 8, (n, k)).astype(np.int8)
+    q[0, :16] = np.arange(-8, 8)
+    s = (r.standard_normal((n, k // d.w_group)) * 0.01).astype(np.float16)
+    packed, scales = _host_pack_codes(fx, d, proj, oracle.pack_nibbles(q), s.view(np.uint16))
+    codes = layouts.decode_weights(packed, n, k)
+    sc = layouts.decode_scales(scales, n, k, d.w_group)
+    if proj == "gateup":
+        codes = layouts.gateup_logical_order(codes, d.intermediate)
+        sc = layouts.gateup_logical_order(sc, d.intermediate)
+    np.testing.assert_array_equal(codes, q)
+    np.testing.assert_array_equal(sc.view(np.uint16), s.view(np.uint16))
+
+
+def test_pack_codes_rejects_non_finite_scale(fx):
+    d = W.TINY
+    n, k = 256, 768
+    s = np.full((n, k // d.w_group), 0.01, np.float16)
+    s[3, 2] = np.inf
+    with pytest.raises(fx.FutxError) as e:
+        _host_pack_codes(fx, d, "down", np.zeros((n, k // 2), np.uint8), s.view(np.uint16))
+    assert e.value.status == fx.FUTX_E_RANGE
+
+
 def test_host_pack_edge_values(fx):
     """Ties, zero groups, fp16-subnormal scales, the -8 code from external
     codes cannot arise; large but representable scales."""

@@ -195,6 +195,33 @@ def test_int4_linear(F, DB, shape, batch):
         assert err <= 1e-5 * np.max(np.abs(ref)) * np.sqrt(kk / 128) + 1e-6, (proj, err)
 
 
+def test_int4_linear_external_codes(F, DB):
+    """Weights that enter as external codes and scales (full code range,
+    -8 included) through futx_pack_codes: the projection equals the fp64
+    product with the dequantized weights."""
+    d = W.LLAMA8B
+    r = np.random.default_rng(41)
+    for proj, (n, kk) in (("o", (4096, 4096)), ("down", (4096, 14336))):
+        q = r.integers(-8, 8, (n, kk)).astype(np.int8)
+        s = (np.abs(r.standard_normal((n, kk // d.w_group))) * 0.003).astype(np.float16)
+        pb, sb = F.futx_packed_sizes(d, proj)
+        packed, scales = DB.device_buffer(pb), DB.device_buffer(sb)
+        F.futx_pack_codes(d, proj, oracle.pack_nibbles(q), s.view(np.uint16), packed, scales)
+        for batch in (1, 8):
+            act = W.to_bf16_values(r.standard_normal((batch, kk)).astype(np.float32))
+            abits = (act.view(np.uint32) >> 16).astype(np.uint16)
+            ws_bytes = F.futx_decode_workspace_size(d, batch, 1)
+            ws = DB.device_buffer(ws_bytes)
+            out = torch.empty((batch, n), dtype=torch.float32, device="cuda")
+            say("int4_linear external codes", proj, "batch", batch)
+            F.futx_int4_linear(d, proj, (packed, scales), batch, torch.from_numpy(abits).cuda(), out, ws, ws_bytes)
+            torch.cuda.synchronize()
+            ref = act.astype(np.float64) @ oracle.dequant_weight(q, s, d.w_group).T
+            err = np.max(np.abs(out.cpu().numpy() - ref))
+            say("  max err %.3g  (max|ref| %.3g)" % (err, np.max(np.abs(ref))))
+            assert err <= 1e-5 * np.max(np.abs(ref)) * np.sqrt(kk / 128) + 1e-6, (proj, batch, err)
+
+
 # ---------------------------------------------------------------- attention
 
 
@@ -290,3 +317,57 @@ def test_block_70b(batch):
     """Llama-3-70B-shape block (hidden 8192, 64/8 heads, intermediate 28672),
     4096 cached tokens per sequence."""
     _check_block(BlockCase(W.llama70b(batch)), reps=1)
+
+
+@pytest.mark.parametrize("shape,lens", [("tiny", [61, 0, 127]), ("8b", [62, 300])])
+def test_multi_step_decode(F, DB, shape, lens):
+    """Several decode steps in a row on one cache: each step appends its new
+    token at slot cached_lens[b] (crossing page boundaries into pages drawn
+    from a seeded permutation), the caller then advances cached_lens, and
+    the next step attends to every token written so far.  Each step's output
+    is checked against the oracle block continuing on its own cache (the
+    new token's boundary-case codes taken from the device, as in the
+    single-block tests)."""
+    from tests.gpu_common import cache_tokens
+
+    steps = 4
+    dims = W.TINY if shape == "tiny" else W.LLAMA8B
+    wl = W.Workload(f"multistep-{shape}", dims, len(lens), "fixed:0")
+    d = wl.dims
+    lens = np.asarray(lens, np.int32)
+    layout = W.page_layout(wl, lens, extra_tokens=steps, seed=0, spare_pages=1)
+    w = W.block_weights(wl, 0)
+    hist = [W.history(wl, 0, b, int(L)) for b, L in enumerate(lens)]
+    layer = DB.DeviceLayer(d, w)
+    cache = DB.DeviceKVCache(d, layout.num_pages)
+    for b, (k, v) in enumerate(hist):
+        DB.fill_history(cache, k, v, layout, b)
+    qw = oracle.quantize_block_weights(w, d)
+    ocaches = []
+    for b, (k, v) in enumerate(hist):
+        c = oracle.LogicalKVCache.empty(int(lens[b]) + steps, d.n_kv_heads, d.head_dim)
+        if lens[b]:
+            oracle.history_fill(c, k, v, np.arange(int(lens[b])), d)
+        ocaches.append(c)
+    for t in range(steps):
+        cur = lens + t
+        x = W.hidden_state(wl, tag=f"x{t}")
+        runner = DB.DecodeRunner(d, wl.batch, cur, layout.block_table)
+        xd = torch.from_numpy(x.copy()).cuda()
+        say("multi-step decode", shape, "step", t, "cached_lens", cur.tolist())
+        runner.decode(layer, cache, xd)
+        torch.cuda.synchronize()
+        got = xd.cpu().numpy()
+        slots = np.array([layout.slot(b, int(L)) for b, L in enumerate(cur)], np.int32)
+        K, KS, V, VS = cache_tokens(cache.host_copy(), d, layout.num_pages, slots)
+
+        def hook(b, kc, ks, vc, vs, k_rot, v_rot):
+            _flip_tolerant(K[b], KS[b], np.asarray(k_rot, np.float64), ("new key", t, b), max_frac=1.0)
+            _flip_tolerant(V[b], VS[b], np.asarray(v_rot, np.float64), ("new value", t, b), max_frac=1.0)
+            return K[b].astype(kc.dtype), KS[b].astype(ks.dtype), V[b].astype(vc.dtype), VS[b].astype(vs.dtype)
+
+        ref = oracle.decode_block(x, qw, ocaches, cur, d, kv_hook=hook)
+        err = float(np.max(np.abs(got - ref)))
+        tol = block_tolerance(ref)
+        say("  step %d max err %.3g tol %.3g" % (t, err, tol))
+        assert err <= tol, (t, err, tol)
