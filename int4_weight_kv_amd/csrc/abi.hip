@@ -77,7 +77,7 @@ futx_status check_proj(futx_proj p) {
 // ---------------------------------------------------------------- workspace
 
 struct Ws {
-  uint16_t* act;   // 3 x [32][Kmax] bf16 (GEMM operand; three terms for the O projection)
+  uint16_t* act;   // 3 x [32][Kmax] bf16 (GEMM operand; FUTX_O_TERMS terms for the O projection)
   float2* gsum;    // [Kmax / G][32] exact group sums as (hi, lo)
   float* invr;     // [32]
   float* invr2;    // [32]
@@ -99,7 +99,7 @@ static size_t part_floats(const futx_dims& d, int B) {
   size_t m = 0;
   for (int p = 0; p < 4; ++p) {
     ProjShape s = proj_shape(d, (futx_proj)p);
-    GemmPlan2 g = plan_gemm(s.n, s.k, d.w_group, B, p == FUTX_PROJ_O ? 3 : 1, kEpiPartial);
+    GemmPlan2 g = plan_gemm(s.n, s.k, d.w_group, B, p == FUTX_PROJ_O ? FUTX_O_TERMS : 1, kEpiPartial);
     size_t v = (size_t)g.splits * B * s.n;
     if (v > m) m = v;
   }
@@ -362,14 +362,14 @@ static futx_status decode_block_impl(const futx_dims* dims, const futx_block_wei
     STEP(launch_attn_decode(ws.qkv, cached_lens, block_table, max_pages_per_seq, B, nq, D, ap, d.had_block,
                             d.rope_theta, kv, ws.apart, s));
   // ... then the merge of the workgroup partials, inverse rotation -> the O
-  // projection operand (three bf16 terms)
+  // projection operand (FUTX_O_TERMS bf16 terms)
   AttnPlan apw;
   apw.chunk = 4 * ap.chunk;
   apw.nsplit = (ap.nsplit + 3) / 4;
   if (run(FUTX_STAGE_MERGE))
     STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, apw, d.had_block, nullptr, ws.act, term, s));
   // O projection + residual: h = x + O(o)
-  if (run(FUTX_STAGE_O)) STEP(gemm(w->o, H, nq * D, ws.act, 3, false, kEpiResid, x, ws.h, nullptr));
+  if (run(FUTX_STAGE_O)) STEP(gemm(w->o, H, nq * D, ws.act, FUTX_O_TERMS, false, kEpiResid, x, ws.h, nullptr));
   // RMSNorm-2 + gate/up + SwiGLU -> bf16 activation
   if (run(FUTX_STAGE_GATEUP)) STEP(gemm(w->gateup, 2 * I, H, ws.h, 1, true, kEpiSwiglu, nullptr, nullptr, ws.act));
   // down projection + residual: x = h + down(act)

@@ -5,6 +5,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// bf16 terms of the O projection operand: the attention output o enters
+// the matrix cores as hi + lo with hi = bf16(o), lo = bf16(o - hi), so
+// |o - hi - lo| <= 2^-18 |o| (three terms would carry it to fp32 accuracy;
+// measured on MI355X, two terms halve the O projection at batch 8 and above,
+// with every block parity case still within tolerance)
+#ifndef FUTX_O_TERMS
+#define FUTX_O_TERMS 2
+#endif
+
 namespace futx {
 
 // LDS budget of a workgroup's staged activation range (two workgroups per

@@ -552,13 +552,13 @@ hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi
   } while (0)
   switch (epi) {
     case kEpiPartial:
-      if (nterms == 3) FUTX_GRP(3, false, kEpiPartial, 0);
+      if (nterms == FUTX_O_TERMS) FUTX_GRP(FUTX_O_TERMS, false, kEpiPartial, 0);
       else if (act_f32) FUTX_GRP(1, true, kEpiPartial, 0);
       else FUTX_GRP(1, false, kEpiPartial, 0);
       break;
     case kEpiRms: FUTX_GRP(1, true, kEpiRms, 0); break;
     case kEpiResid:
-      if (nterms == 3) FUTX_GRP(3, false, kEpiResid, 0); else FUTX_GRP(1, false, kEpiResid, 0);
+      if (nterms == FUTX_O_TERMS) FUTX_GRP(FUTX_O_TERMS, false, kEpiResid, 0); else FUTX_GRP(1, false, kEpiResid, 0);
       break;
     case kEpiSwiglu: FUTX_GRP(1, true, kEpiSwiglu, 1); break;
     default: return hipErrorInvalidValue;

@@ -52,7 +52,7 @@ hipError_t launch_attention(const void* q, bool q_f32, const int32_t* lens, int 
                             const int32_t* block_table, int mpps, int B, int nq, int D,
                             const AttnPlan& plan, const KVPtrsConst& kv, float* apart,
                             hipStream_t st);
-// out_bf16: three bf16 terms of o, term t at out_bf16 + t * term_stride
+// out_bf16: FUTX_O_TERMS bf16 terms of o (gemm.h), term t at out_bf16 + t * term_stride
 hipError_t launch_attn_merge(const float* apart, const int32_t* lens, int len_add, int B, int nq,
                              int D, const AttnPlan& plan, int hb, float* out_f32,
                              uint16_t* out_bf16, size_t term_stride, hipStream_t st);

@@ -7,6 +7,7 @@
 // registers and fed to the matrix cores, a rotated INT4 KV cache, and
 // split-sequence decode attention.  Operand and cache layouts: layout.h.
 #include "device.h"
+#include "gemm.h"
 #include "futx.h"
 #include "kernels.h"
 
@@ -433,20 +434,32 @@ __device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x
         for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
       }
   };
-  int page = bt[t0 / kPageSize];
-  auto step = [&](int pt, bool first) {
-    const int page_next = bt[min(pt + kPageSize, t1 - 1) / kPageSize];
-    Blk r0, r1;
-    load_blk(page, pt % kPageSize, r0);
-    const bool two = pt + 32 < t1 && (pt % kPageSize) == 0;
-    load_blk(page, two ? 32 : pt % kPageSize, r1);
-    if (first) make_q();
-    compute_blk(pt, r0);
-    if (two) compute_blk(pt + 32, r1);
-    page = page_next;
+  // Pages are double-buffered: the loads of page i + 1 are issued before
+  // page i is computed (t0 is page-aligned: splits are whole pages).  Past
+  // the last page the loads repeat it (valid addresses) and are not used.
+  auto issue = [&](int pt, Blk& r0, Blk& r1) {
+    const int pg = bt[min(pt, t1 - 1) / kPageSize];
+    load_blk(pg, 0, r0);
+    load_blk(pg, 32, r1);
   };
-  step(t0, true);  // first page peeled: the query work overlaps its loads
-  for (int pt = t0 + kPageSize - t0 % kPageSize; pt < t1; pt += kPageSize) step(pt, false);
+  auto consume = [&](int pt, const Blk& r0, const Blk& r1) {
+    compute_blk(pt, r0);
+    if (pt + 32 < t1) compute_blk(pt + 32, r1);
+  };
+  Blk a0, a1, b0, b1;
+  int pt = t0;
+  issue(pt, a0, a1);
+  make_q();  // the query work overlaps the first page's loads
+  for (;;) {
+    issue(pt + kPageSize, b0, b1);
+    consume(pt, a0, a1);
+    pt += kPageSize;
+    if (pt >= t1) break;
+    issue(pt + kPageSize, a0, a1);
+    consume(pt, b0, b1);
+    pt += kPageSize;
+    if (pt >= t1) break;
+  }
 }
 
 template <int D, bool QF32>
@@ -549,16 +562,18 @@ __device__ __forceinline__ void q_hop(float (&qv)[D / 32][8], int lane) {
     }
 }
 
-// o (fp32, channel c of query head i) -> the O projection operand: three
-// bf16 terms hi + mid + lo (24 significant bits), term t at out + t * stride.
-__device__ __forceinline__ void store_three_terms(float o, uint16_t* out, size_t at, size_t term_stride) {
-  const uint16_t t0 = f32_to_bf16_bits(o);
-  const float r1 = o - bf16_bits_to_f32(t0);
-  const uint16_t t1 = f32_to_bf16_bits(r1);
-  const uint16_t t2 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(t1));
-  out[at] = t0;
-  out[at + term_stride] = t1;
-  out[at + 2 * term_stride] = t2;
+// o (fp32, channel c of query head i) -> the O projection operand: NT bf16
+// terms, each the bf16 rounding of what the terms before it leave (two
+// terms: 16 significant bits; three: 24), term t at out + t * stride.
+template <int NT>
+__device__ __forceinline__ void store_terms(float o, uint16_t* out, size_t at, size_t term_stride) {
+  float r = o;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint16_t v = f32_to_bf16_bits(r);
+    out[at + t * term_stride] = v;
+    r -= bf16_bits_to_f32(v);
+  }
 }
 
 // The attention part of the decode block after the QKV projection, up to
@@ -723,11 +738,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
 // Merge of the split partials + inverse block Hadamard.  One block of D
 // threads per (query head, sequence).  Writes fp32 output, or the operand of
-// the O projection: o as an unevaluated sum of three bf16 terms
+// the O projection: o as an unevaluated sum of FUTX_O_TERMS bf16 terms
 // (hi + mid + lo, 24 significant bits, term t at out_bf16 + t * term_stride)
 // plus the exact group sums of that sum.  The attention output comes out of
 // a long fp32 reduction, so a single bf16 rounding here would flip on tiny
-// differences; three terms carry it at fp32 accuracy.
+// differences; the terms carry it far below bf16's rounding (gemm.h).
 // Cross-split softmax merge of one query head of one sequence, then the
 // inverse block rotation.  256 threads: thread t owns channel chunk t % (D/4)
 // (four channels) for the splits sp = t / (D/4) (mod 256 / (D/4)); all its
@@ -803,8 +818,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   }
   o *= 1.0f / sqrtf((float)hb);
   if (out_f32) out_f32[((size_t)b * nq + i) * D + c] = o;
-  if (out_bf16)  // o as three bf16 terms (hi + mid + lo), the O projection operand
-    store_three_terms(o, out_bf16, (size_t)b * nq * D + (size_t)i * D + c, term_stride);
+  if (out_bf16)  // o as FUTX_O_TERMS bf16 terms, the O projection operand
+    store_terms<FUTX_O_TERMS>(o, out_bf16, (size_t)b * nq * D + (size_t)i * D + c, term_stride);
 }
 
 // ---------------------------------------------------------------- launchers

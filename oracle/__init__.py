@@ -33,7 +33,7 @@ an exact fp32 recipe so that codes can be compared bit for bit, and (ii) the
 bf16 rounding points R1, R3, R4 (R5 for the LM head), where the GPU
 materializes bf16 matrix-core operands; the oracle rounds there too, once,
 from fp64.  (The attention output is not rounded: the GPU passes it to the O
-projection as three bf16 terms.)
+projection as two bf16 terms, relative error at most 2^-18.)
 
 Parity status per function is listed in each module's docstring.  Functions
 with no independent pin say "parity unpinned".

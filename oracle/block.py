@@ -17,8 +17,8 @@ quant, hadamard, rope and attention):
   O9  attention over tokens 0..L_b of the cache (the new token read back
       quantized), inverse rotation of the output.
   O10 h = x + W_o o  (o unrounded: the GPU carries the attention output
-      into the O projection as a sum of three bf16 terms, about fp32
-      accuracy, so there is no bf16 rounding point between attention and
+      into the O projection as a sum of two bf16 terms, relative error at
+      most 2^-18, so there is no bf16 rounding point between attention and
       the O projection)
   O11 RMSNorm-2 like O4: u2 = bf16(h), r2 = sqrt(mean(h^2) + eps)     (R3)
   O12 g = (W_gate u2)/r2, v = (W_up u2)/r2, act = bf16(silu(g) v)    (R4)
