@@ -736,80 +736,90 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 }
 
-// Merge of the split partials + inverse block Hadamard.  One block of D
+// Merge of the split partials + inverse block Hadamard.  One block of 256
 // threads per (query head, sequence).  Writes fp32 output, or the operand of
 // the O projection: o as an unevaluated sum of FUTX_O_TERMS bf16 terms
-// (hi + mid + lo, 24 significant bits, term t at out_bf16 + t * term_stride)
-// plus the exact group sums of that sum.  The attention output comes out of
+// (term t at out_bf16 + t * term_stride).  The attention output comes out of
 // a long fp32 reduction, so a single bf16 rounding here would flip on tiny
 // differences; the terms carry it far below bf16's rounding (gemm.h).
-// Cross-split softmax merge of one query head of one sequence, then the
-// inverse block rotation.  256 threads: thread t owns channel chunk t % (D/4)
-// (four channels) for the splits sp = t / (D/4) (mod 256 / (D/4)); all its
-// accumulator loads are issued before use, so the merge costs a few L2 round
-// trips, not one per split.
+// Thread t owns channel chunk t % (D/4) (four channels) of the splits
+// sp = t / (D/4) + (256 / (D/4)) u.  The partials were written by the
+// previous kernel on other CUs, so every load of a round (U splits per
+// thread) is issued before any is used, and before the sequence length is
+// known (indices clamped to the workspace's splits, the extra ones masked
+// out afterwards): one round trip per 256 / (D/4) * U splits.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float* __restrict__ apart, const int32_t* __restrict__ lens, int len_add, int nq,
     int chunk, int nsplit, int hb, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
     size_t term_stride) {
-  constexpr int NC = D / 4;       // float4 chunks per split
-  constexpr int PH = 256 / NC;    // split phases
-  constexpr int MAXW = 1024;      // splits held in LDS
-  __shared__ float s_w[MAXW];
+  constexpr int NC = D / 4;     // float4 chunks per split
+  constexpr int PH = 256 / NC;  // split phases
+  constexpr int U = 4;          // splits per thread and round
+  __shared__ float s_m[PH], s_l[PH];
   __shared__ float4 s_acc[PH][NC];
-  __shared__ float s_red[4], s_l;
-  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int L = lens[b] + len_add;
-  const int nsp = min((L + chunk - 1) / chunk, nsplit);
-  const float* base = apart + ((size_t)b * nq + i) * nsplit * (D + 2);
-  // running max over the splits
-  float m = -INFINITY;
-  for (int sp = t; sp < nsp; sp += 256) m = fmaxf(m, base[(size_t)sp * (D + 2)]);
-  m = wave_max(m);
-  if (lane == 0) s_red[wv] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();
-  float l = 0.f;
-  for (int sp = t; sp < nsp; sp += 256) {
-    const float w = expf(base[(size_t)sp * (D + 2)] - M);
-    if (sp < MAXW) s_w[sp] = w;
-    l += w * base[(size_t)sp * (D + 2) + 1];
-  }
-  l = wave_sum(l);
-  if (lane == 0) s_red[wv] = l;
-  __syncthreads();
-  if (t == 0) s_l = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-  // weighted accumulators: 8 loads in flight per thread and batch
+  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63;
   const int ch = t % NC, ph = t / NC;
+  const float* base = apart + ((size_t)b * nq + i) * nsplit * (D + 2);
+  const int L = lens[b] + len_add;
+  float m = -INFINITY, l = 0.f;
   float4 a = {0.f, 0.f, 0.f, 0.f};
-  for (int sp0 = ph; sp0 < nsp; sp0 += 8 * PH) {
-    float4 v[8];
+  int nsp = nsplit;  // known after the first round's loads are issued
+  for (int r0 = 0; r0 < nsp; r0 += PH * U) {
+    float mv[U], lv[U];
+    float4 av[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int sp = min(sp0 + u * PH, nsp - 1);
-      v[u] = *(const float4*)(base + (size_t)sp * (D + 2) + 2 + 4 * ch);
+    for (int u = 0; u < U; ++u) {
+      const float* pw = base + (size_t)min(r0 + ph + PH * u, nsplit - 1) * (D + 2);
+      mv[u] = pw[0];
+      lv[u] = pw[1];
+      av[u] = *(const float4*)(pw + 2 + 4 * ch);
     }
+    nsp = min((L + chunk - 1) / chunk, nsplit);
+    bool ok[U];
+    float mr = m;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int sp = sp0 + u * PH;
-      const float w = sp < nsp ? (sp < MAXW ? s_w[sp] : expf(base[(size_t)sp * (D + 2)] - M)) : 0.f;
-      a.x = fmaf(w, v[u].x, a.x);
-      a.y = fmaf(w, v[u].y, a.y);
-      a.z = fmaf(w, v[u].z, a.z);
-      a.w = fmaf(w, v[u].w, a.w);
+    for (int u = 0; u < U; ++u) {
+      ok[u] = r0 + ph + PH * u < nsp;
+      if (ok[u]) mr = fmaxf(mr, mv[u]);
     }
+    if (mr == -INFINITY) continue;  // no split of this phase in the round
+    const float sc = m == -INFINITY ? 0.f : expf(m - mr);
+    l *= sc;
+    a.x *= sc; a.y *= sc; a.z *= sc; a.w *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = ok[u] ? expf(mv[u] - mr) : 0.f;
+      if (ok[u]) {  // select: a stale partial never enters, not even times 0
+        l = fmaf(w, lv[u], l);
+        a.x = fmaf(w, av[u].x, a.x);
+        a.y = fmaf(w, av[u].y, a.y);
+        a.z = fmaf(w, av[u].z, a.z);
+        a.w = fmaf(w, av[u].w, a.w);
+      }
+    }
+    m = mr;
+  }
+  if (ch == 0) {
+    s_m[ph] = m;
+    s_l[ph] = l;
   }
   s_acc[ph][ch] = a;
   __syncthreads();
   if (t >= D) return;
-  // channel c = t: sum over the phases in a fixed order
+  // channel c = t: the phases merged in a fixed order (phase 0 always holds
+  // split 0, so M is finite)
   const int c = t;
-  float o = 0.f;
+  float M = -INFINITY;
 #pragma unroll
-  for (int p = 0; p < PH; ++p) o += ((const float*)&s_acc[p][c / 4])[c % 4];
-  const float ltot = s_l;
+  for (int p = 0; p < PH; ++p) M = fmaxf(M, s_m[p]);
+  float o = 0.f, ltot = 0.f;
+#pragma unroll
+  for (int p = 0; p < PH; ++p) {
+    const float w = s_m[p] == -INFINITY ? 0.f : expf(s_m[p] - M);
+    o = fmaf(w, ((const float*)&s_acc[p][c / 4])[c % 4], o);
+    ltot = fmaf(w, s_l[p], ltot);
+  }
   o = ltot > 0.f ? o / ltot : 0.f;
   // inverse rotation (the normalized Sylvester matrix is its own inverse)
   for (int hop = 1; hop < hb; hop <<= 1) {
