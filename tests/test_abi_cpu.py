@@ -196,6 +196,21 @@ def test_pack_codes_rejects_non_finite_scale(fx):
     assert e.value.status == fx.FUTX_E_RANGE
 
 
+def test_pack_codes_rejects_null_and_bad_projection(fx):
+    d = W.TINY
+    pb, sb = fx.futx_packed_sizes(d, "down")
+    packed, scales = np.zeros(pb, np.uint8), np.zeros(sb // 2, np.uint16)
+    sc = np.zeros((256, 12), np.uint16)
+    # null codes pointer, through the C entry point directly
+    st = fx._lib.futx_pack_codes_host(fx.ctypes.byref(fx.make_dims(d)), fx.FUTX_PROJ_DOWN, None, fx._ptr(sc),
+                                      fx._ptr(packed), fx._ptr(scales))
+    assert st == fx.FUTX_E_ARG
+    with pytest.raises(fx.FutxError) as e:
+        fx._check("futx_pack_codes_host", fx._lib.futx_pack_codes_host(
+            fx.ctypes.byref(fx.make_dims(d)), 7, None, None, None, None))
+    assert e.value.status == fx.FUTX_E_ARG
+
+
 def test_host_pack_edge_values(fx):
     """Ties, zero groups, fp16-subnormal scales, the -8 code from external
     codes cannot arise; large but representable scales."""
