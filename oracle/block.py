@@ -33,10 +33,17 @@ Everything is fp64 except the quantizers (fp32 recipe) and the bf16
 rounding points R1 (block input), R3 (MLP input), R4 (SwiGLU output) and R5
 (LM-head input), where the GPU materializes bf16 matrix-core operands.
 
-Parity status: the parts are pinned in tests/test_oracle_*.py; the composed
-block is checked against ``decode_block_unquantized`` (differences of
-quantization-noise size only), which is a sanity check, not a pin:
-whole-block composition is "parity unpinned" beyond its parts.
+Parity status.  The parts are pinned in tests/test_oracle_pins.py.  The
+composition is pinned in tests/test_oracle_closed_forms.py by closed forms:
+a constant input row fixes qkv, g and up as bf16(c) times row sums of the
+dequantized weights over sqrt(c^2 + eps) (O4/O5, O11/O12); zero O weights
+make h = x; eps = 0 makes qkv, g and up invariant under x -> 2^k x; unit
+head rows fix the logits and the lowest-index top-1 (O15 tail); zero
+projections reduce the step to the head of the embedding row (O15).  The
+attention output's path into h (O9 -> O10) and the new token's append are
+covered by the attention pins and by the comparison with
+``decode_block_unquantized`` (quantization-noise-sized differences only),
+which is a sanity check rather than an exact pin.
 """
 
 from dataclasses import dataclass, field

@@ -10,7 +10,8 @@ Readings: Sylvester construction in natural order, H_n[i][j] =
 symmetric and its own inverse; no random signs; the blocks are contiguous
 runs of ``hb`` channels of one head (hb = 32 or 64).
 
-Pins (tests/test_oracle_hadamard.py): H H^T = n I exactly in integers for
+Pins (tests/test_oracle_pins.py, tests/golden/hadamard_cases.txt): H H^T =
+n I exactly in integers for
 n = 32 and 64; equality with scipy.linalg.hadamard (a library routine);
 symmetry and involution of the normalized matrix; the hand value
 Hn_64 (16 e_0) = (2, ..., 2); invariance of dot products under the same

@@ -18,9 +18,12 @@ Readings (the pages give no format details):
   and code 2i+1 in its high nibble, two's complement;
 * fold first, then quantize: W' = fp32(W * gain[k]), one fp32 multiply.
 
-Pins (tests/test_oracle_quant.py, tests/golden/quant_cases.txt): hand cases
+Pins (tests/test_oracle_pins.py with tests/golden/quant_cases.txt and
+tests/golden/pack_cases.txt; tests/test_oracle_closed_forms.py): hand cases
 with exact expected codes/scales, the round-trip bound |w - q*s| <= s/2,
-packing hand cases and an exhaustive byte round trip.
+packing hand cases and an exhaustive byte round trip; folding with
+power-of-two gains per group leaves the codes unchanged and multiplies each
+group scale by its power of two.
 """
 
 import numpy as np

@@ -9,7 +9,8 @@ no frequency scaling, angle p * theta_i computed in fp64.
     (a, b) -> (a cos(p th_i) - b sin(p th_i),  b cos(p th_i) + a sin(p th_i))
     with a = x[i], b = x[i + d/2]
 
-Pins (tests/test_oracle_rope.py): p = 0 is the identity; pair norms are
+Pins (tests/test_oracle_pins.py, tests/golden/rope_cases.txt): p = 0 is the
+identity; pair norms are
 preserved; (R_m q).(R_n k) depends on m - n only; a hand-computed d = 4 case.
 """
 
