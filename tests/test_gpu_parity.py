@@ -16,7 +16,7 @@ import pytest
 import oracle
 from int4_weight_kv_amd import workload as W
 from tests import layouts
-from tests.gpu_common import BlockCase, block_tolerance, cache_tokens, flip_tolerant, say
+from tests.gpu_common import BlockCase, FlipStats, block_tolerance, cache_tokens, flip_tolerant, say
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -123,9 +123,9 @@ def test_kv_append_full_chain(F, DB, shape):
     torch.cuda.synchronize()
     K, KS, V, VS = _cache_tokens(cache.host_copy(), d, num_pages, slots)
     kr, vr = oracle.rotate_kv(k.astype(np.float64), v.astype(np.float64), pos[:, None], d)
-    fk = _flip_tolerant(K, KS, kr, "keys")
-    fv = _flip_tolerant(V, VS, vr, "values")
-    say("boundary flips (codes, scales): keys", fk, "values", fv)
+    fk = _flip_tolerant(K, KS, kr, "keys", max_per_row=1)
+    fv = _flip_tolerant(V, VS, vr, "values", max_per_row=1)
+    say("boundary decisions: keys", fk, "; values", fv)
 
 
 def test_kv_append_rotation_ablation(F, DB):
@@ -275,8 +275,9 @@ def _check_block(case, reps=2):
         np.testing.assert_array_equal(o, outs[0])  # deterministic: bitwise repeatable
     err = float(np.max(np.abs(outs[0] - y)))
     tol = block_tolerance(y)
-    say(case.wl.name, "block max err %.4g tol %.4g" % (err, tol))
-    assert err <= tol
+    say(case.wl.name, "block max err %.4g tol %.4g (%.3f of tol); %d runs bitwise equal; new token: %s"
+        % (err, tol, err / tol, reps, case.kv_flips))
+    assert err <= tol, (case.wl.name, err, tol, str(case.kv_flips))
     return outs[0], y
 
 
@@ -308,7 +309,18 @@ def test_block_8b():
 
 @pytest.mark.parametrize("batch", [1, 4, 8, 16, 32])
 def test_block_8b_ragged_outliers(batch):
-    _check_block(BlockCase(W.llama8b_ragged(batch)), reps=1)
+    # batch 32 (split-K projections and their reduce kernels) runs twice and
+    # must repeat bit for bit
+    _check_block(BlockCase(W.llama8b_ragged(batch)), reps=2 if batch == 32 else 1)
+
+
+@pytest.mark.parametrize("shape,x_scale", [("tiny", 8.0), ("tiny", 1.0 / 16), ("8b", 8.0), ("8b", 1.0 / 16)])
+def test_block_input_far_from_unit_rms(shape, x_scale):
+    """Block inputs with RMS 8 and 1/16 instead of about 1: the RMSNorm scale
+    1/r enters the QKV and gate/up epilogues, so a misapplied scale shows up
+    here even where unit-RMS inputs would hide it."""
+    wl = W.tiny(2) if shape == "tiny" else W.llama8b(1)
+    _check_block(BlockCase(wl, x_scale=x_scale), reps=1)
 
 
 @pytest.mark.slow
@@ -316,7 +328,7 @@ def test_block_8b_ragged_outliers(batch):
 def test_block_70b(batch):
     """Llama-3-70B-shape block (hidden 8192, 64/8 heads, intermediate 28672),
     4096 cached tokens per sequence."""
-    _check_block(BlockCase(W.llama70b(batch)), reps=1)
+    _check_block(BlockCase(W.llama70b(batch)), reps=2 if batch == 8 else 1)
 
 
 @pytest.mark.parametrize("shape,lens", [("tiny", [61, 0, 127]), ("8b", [62, 300])])
@@ -361,13 +373,17 @@ def test_multi_step_decode(F, DB, shape, lens):
         slots = np.array([layout.slot(b, int(L)) for b, L in enumerate(cur)], np.int32)
         K, KS, V, VS = cache_tokens(cache.host_copy(), d, layout.num_pages, slots)
 
+        flips = FlipStats()
+
         def hook(b, kc, ks, vc, vs, k_rot, v_rot):
-            _flip_tolerant(K[b], KS[b], np.asarray(k_rot, np.float64), ("new key", t, b), max_frac=1.0)
-            _flip_tolerant(V[b], VS[b], np.asarray(v_rot, np.float64), ("new value", t, b), max_frac=1.0)
+            flips.add(_flip_tolerant(K[b], KS[b], np.asarray(k_rot, np.float64), ("new key", t, b), max_frac=1.0,
+                                     max_per_row=1))
+            flips.add(_flip_tolerant(V[b], VS[b], np.asarray(v_rot, np.float64), ("new value", t, b), max_frac=1.0,
+                                     max_per_row=1))
             return K[b].astype(kc.dtype), KS[b].astype(ks.dtype), V[b].astype(vc.dtype), VS[b].astype(vs.dtype)
 
         ref = oracle.decode_block(x, qw, ocaches, cur, d, kv_hook=hook)
         err = float(np.max(np.abs(got - ref)))
         tol = block_tolerance(ref)
-        say("  step %d max err %.3g tol %.3g" % (t, err, tol))
+        say("  step %d max err %.3g tol %.3g; new token: %s" % (t, err, tol, flips))
         assert err <= tol, (t, err, tol)
