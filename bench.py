@@ -384,15 +384,13 @@ def main():
 
     if args.phase == "stages":
         # per-stage times (futx_decode_block_stage), each stage replayed alone
-        # from a graph over the cycled layers; stage 1 runs inside stage 2
-        names = ["qkv", "rotate_append", "attention", "merge", "o", "gateup", "down"]
+        # from a graph over the cycled layers
+        names = ["qkv", "attention", "o", "gateup", "down"]
         res = {"phase": "stages", "workload": args.workload, "batch": int(wl.batch), "layers": nl, "unit": "us"}
         g_blk = capture(block, 4 * nl)
         ms, n = timed([(g_blk, 4 * nl)], max(1, args.steps // (4 * nl)))
         res["block"] = round(ms * 1e3 / n, 2)
         for si, nm in enumerate(names):
-            if nm == "rotate_append":
-                continue
             fn = lambda i, si=si: runner.stage(layers[i % nl], caches[i % nl], x, si)
             g = capture(fn, 4 * nl)
             with torch.cuda.stream(stream):

@@ -216,23 +216,27 @@ futx_status futx_decode_workspace_size(const futx_dims* dims, int32_t max_batch,
  *   workspace   >= futx_decode_workspace_size(dims, batch, max context) bytes
  *               (dev), contents need not be initialized.
  *   max_context upper bound on cached_lens[b] + 1 over the batch (sizes the
- *               split-sequence attention); must be <= the workspace's. */
+ *               split-sequence attention); must be <= the workspace's.  A
+ *               sequence outside it (or with cached_lens[b] < 0) is not
+ *               written to the cache and its row of x becomes NaN (the
+ *               kernels stay in bounds). */
 futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
                               float* x, const int32_t* cached_lens, const int32_t* block_table,
                               int32_t max_pages_per_seq, int32_t max_context,
                               const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Stages of futx_decode_block, in launch order. */
-#define FUTX_STAGE_QKV 0            /* RMSNorm-1 scale + QKV projection */
-#define FUTX_STAGE_ROTATE_APPEND 1  /* (inside the attention kernel: launches nothing) */
-#define FUTX_STAGE_ATTENTION 2      /* one kernel: RoPE, block rotation and INT4 append of the new
-                                       token, rotated queries, split-sequence attention partials */
-#define FUTX_STAGE_MERGE 3          /* cross-split merge + inverse rotation */
-#define FUTX_STAGE_O 4              /* O projection + residual 1 */
-#define FUTX_STAGE_GATEUP 5         /* RMSNorm-2 scale + gate/up projection + SwiGLU */
-#define FUTX_STAGE_DOWN 6           /* down projection + residual 2 */
-#define FUTX_STAGE_COUNT 7
+/* Stages of futx_decode_block, in launch order (one kernel each; the
+ * attention stage adds a merge kernel when the plan splits a sequence over
+ * more than one workgroup). */
+#define FUTX_STAGE_QKV 0        /* RMSNorm-1 scale + QKV projection */
+#define FUTX_STAGE_ATTENTION 1  /* RoPE, block rotation and INT4 append of the new token, rotated
+                                   queries, split-sequence attention, merge of the splits and the
+                                   inverse rotation */
+#define FUTX_STAGE_O 2          /* O projection + residual 1 */
+#define FUTX_STAGE_GATEUP 3     /* RMSNorm-2 scale + gate/up projection + SwiGLU */
+#define FUTX_STAGE_DOWN 4       /* down projection + residual 2 */
+#define FUTX_STAGE_COUNT 5
 
 /* Runs one stage of futx_decode_block with the same kernels, launch
  * configuration and workspace, for per-kernel timing (same arguments, plus
@@ -257,13 +261,22 @@ futx_status futx_int4_linear(const futx_dims* dims, futx_proj proj, const futx_q
                              int32_t batch, const uint16_t* act, float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Decode attention alone: for query head i of sequence b, attend over cache
- * positions 0..lens[b]-1 (note: lens counts every token to read) of KV head
- * i / (n_heads / n_kv_heads), softmax(q k / sqrt(head_dim)) v, then the
- * inverse block-Hadamard rotation [ABS, INT4].  q_rot: bf16 [batch][n_heads]
- * [head_dim] rotated queries (dev); out: fp32 [batch][n_heads][head_dim]. */
-futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const uint16_t* q_rot,
-                                  const int32_t* lens, const int32_t* block_table,
+/* The attention stage of futx_decode_block alone, with the same kernel and
+ * launch configuration, writing fp32 instead of the O-projection operand
+ * [ABS, INT4]: for each sequence b and KV head, the new token's key gets
+ * RoPE at position cached_lens[b], its key and value the block-Hadamard
+ * rotation; both are quantized per token and written to the cache at slot
+ * cached_lens[b]; then query head i attends over positions
+ * 0..cached_lens[b] of KV head i / (n_heads / n_kv_heads) with rotated
+ * queries, softmax(q k / sqrt(head_dim)) v, and the output is rotated back.
+ *   qkv     fp32 [batch][(n_heads + 2 n_kv_heads) head_dim] (dev): the QKV
+ *           projection, rows q | k | v head-major, before RoPE.
+ *   out     fp32 [batch][n_heads][head_dim] (dev).
+ *   other arguments as futx_decode_block.
+ * A sequence with cached_lens[b] < 0 or cached_lens[b] + 1 > max_context
+ * gets NaN outputs and no cache write (the kernels stay in bounds). */
+futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const float* qkv,
+                                  const int32_t* cached_lens, const int32_t* block_table,
                                   int32_t max_pages_per_seq, int32_t max_context,
                                   const futx_kv_cache* cache, float* out, void* workspace,
                                   size_t workspace_bytes, void* stream);

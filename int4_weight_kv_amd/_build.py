@@ -1,7 +1,8 @@
 """Builds libfutx.so (HIP for gfx950 + host C++) in the package directory.
 
-Usage: python -m int4_weight_kv_amd._build   (or __graft_entry__.build()).
-Always recompiles every source.
+Usage: python -m int4_weight_kv_amd._build [--changed]   (or __graft_entry__.build()).
+Recompiles every source; with --changed, only sources whose object is older
+than the source or any header.
 """
 
 import os
@@ -43,18 +44,31 @@ def _run(cmd):
     return r
 
 
-def build(verbose=False):
+def _stale(src, obj):
+    if not os.path.exists(obj):
+        return True
+    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    heads += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    newest = max(os.path.getmtime(f) for f in [src] + heads)
+    return os.path.getmtime(obj) < newest
+
+
+def build(verbose=False, changed_only=False):
     os.makedirs(BUILD, exist_ok=True)
-    jobs = []
-    for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    for src in CPP_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
-        jobs.append([shutil.which("g++") or "g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        list(ex.map(_run, jobs))
-    objs = [j[-1] for j in jobs]
+    jobs, objs = [], []
+    for src in HIP_SOURCES + CPP_SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        if changed_only and not _stale(path, obj):
+            continue
+        if src.endswith(".hip"):
+            jobs.append([HIPCC, *HIP_FLAGS, "-c", path, "-o", obj])
+        else:
+            jobs.append([shutil.which("g++") or "g++", *CXX_FLAGS, "-c", path, "-o", obj])
+    if jobs:
+        with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+            list(ex.map(_run, jobs))
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs])
     os.replace(tmp, LIB)
@@ -64,4 +78,4 @@ def build(verbose=False):
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, changed_only="--changed" in sys.argv[1:])

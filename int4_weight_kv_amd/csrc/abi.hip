@@ -78,12 +78,11 @@ futx_status check_proj(futx_proj p) {
 
 struct Ws {
   uint16_t* act;   // 3 x [32][Kmax] bf16 (GEMM operand; FUTX_O_TERMS terms for the O projection)
-  float2* gsum;    // [Kmax / G][32] exact group sums as (hi, lo)
   float* invr;     // [32]
   float* invr2;    // [32]
   float* part;     // split-K partials
   float* qkv;      // [B][Nqkv]
-  float* apart;    // [B][nq][nsplit][D + 2]
+  float* apart;    // [B][nq][workgroups per sequence][D + 2] attention partials
   float* h;        // [B][H]
   size_t bytes;
 };
@@ -117,14 +116,14 @@ static Ws carve(const futx_dims& d, int B, int max_ctx, char* base) {
   const int K = kmax(d);
   const int D = d.head_dim, nq = d.n_heads;
   const int nqkv = (d.n_heads + 2 * d.n_kv_heads) * D;
-  const int nsplit = (max_ctx + kPageSize - 1) / kPageSize;  // chunk >= one page
+  // attention workgroups per sequence, for any context up to max_ctx
+  const int nwg = (attn_nsplit_bound(B, d.n_kv_heads, max_ctx) + 3) / 4;
   w.act = (uint16_t*)take((size_t)3 * kMaxBatch * K * 2);
-  w.gsum = (float2*)take((size_t)(K / d.w_group) * kMaxBatch * 8);
   w.invr = (float*)take(kMaxBatch * 4);
   w.invr2 = (float*)take(kMaxBatch * 4);
   w.part = (float*)take(part_floats(d, B) * 4);
   w.qkv = (float*)take((size_t)B * nqkv * 4);
-  w.apart = (float*)take((size_t)B * nq * (nsplit < 1 ? 1 : nsplit) * (D + 2) * 4);
+  w.apart = (float*)take((size_t)B * nq * nwg * (D + 2) * 4);
   w.h = (float*)take((size_t)B * d.hidden * 4);
   w.bytes = at;
   return w;
@@ -133,11 +132,6 @@ static Ws carve(const futx_dims& d, int B, int max_ctx, char* base) {
 static KVPtrs kv_ptrs(const futx_kv_cache* c, int nkv) {
   return KVPtrs{(uint8_t*)c->k_codes, (uint8_t*)c->v_codes, (uint16_t*)c->k_scales,
                 (uint16_t*)c->v_scales, nkv};
-}
-
-static KVPtrsConst kv_cptrs(const futx_kv_cache* c, int nkv) {
-  return KVPtrsConst{(const uint8_t*)c->k_codes, (const uint8_t*)c->v_codes,
-                     (const uint16_t*)c->k_scales, (const uint16_t*)c->v_scales, nkv};
 }
 
 static futx_status check_cache(const futx_kv_cache* c) {
@@ -275,12 +269,27 @@ futx_status futx_decode_workspace_size(const futx_dims* dims, int32_t max_batch,
   if (st) return st;
   if (max_batch < 1 || max_batch > kMaxBatch || max_context < 1 || !bytes)
     return fail(FUTX_E_ARG, "workspace size: batch must be 1..32 and context >= 1");
-  *bytes = carve(*dims, max_batch, max_context, nullptr).bytes;
+  // the split plan rounds per batch size, so the largest carve over every
+  // batch up to max_batch covers any call with batch <= max_batch
+  size_t m = 0;
+  for (int b = 1; b <= max_batch; ++b) {
+    const size_t v = carve(*dims, b, max_context, nullptr).bytes;
+    if (v > m) m = v;
+  }
+  *bytes = m;
   return FUTX_OK;
 }
 
+}  // extern "C"
+
+namespace futx {
+size_t decode_workspace_bytes(const futx_dims& d, int batch, int max_context) {
+  return carve(d, batch, max_context, nullptr).bytes;
+}
+}  // namespace futx
+
 // stage < 0: every stage in order; otherwise that stage only
-static futx_status decode_block_impl(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+futx_status futx::decode_block_impl(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
                                      float* x, const int32_t* cached_lens, const int32_t* block_table,
                                      int32_t max_pages_per_seq, int32_t max_context,
                                      const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
@@ -348,26 +357,33 @@ static futx_status decode_block_impl(const futx_dims* dims, const futx_block_wei
         return launch_reduce(ws.part, p.splits, B, N, nullptr, resid, out, 0, s);
       case kEpiSwiglu:
         if ((e2 = launch_prep_act((const float*)act, B, K, d.rms_eps, ws.act, ws.invr2, s)) != hipSuccess) return e2;
-        return launch_swiglu(ws.part, p.splits, B, I, G, ws.invr2, out_bf16, ws.gsum, s);
+        return launch_swiglu(ws.part, p.splits, B, I, ws.invr2, out_bf16, s);
     }
     return hipErrorInvalidValue;
   };
   // RMSNorm-1 + QKV (the gain is folded into the weights; 1/r in the epilogue)
   if (run(FUTX_STAGE_QKV)) STEP(gemm(w->qkv, nqkv, H, x, 1, true, kEpiRms, nullptr, ws.qkv, nullptr));
-  // one kernel: RoPE, rotation and INT4 append of the new token, rotated
-  // queries, attention over positions 0..cached_lens[b] in splits, four
-  // splits merged per workgroup (stage ROTATE_APPEND runs inside it) ...
-  const AttnPlan ap = attn_plan(B, d.n_kv_heads, max_context);
-  if (run(FUTX_STAGE_ATTENTION))
-    STEP(launch_attn_decode(ws.qkv, cached_lens, block_table, max_pages_per_seq, B, nq, D, ap, d.had_block,
-                            d.rope_theta, kv, ws.apart, s));
-  // ... then the merge of the workgroup partials, inverse rotation -> the O
-  // projection operand (FUTX_O_TERMS bf16 terms)
-  AttnPlan apw;
-  apw.chunk = 4 * ap.chunk;
-  apw.nsplit = (ap.nsplit + 3) / 4;
-  if (run(FUTX_STAGE_MERGE))
-    STEP(launch_attn_merge(ws.apart, cached_lens, 1, B, nq, D, apw, d.had_block, nullptr, ws.act, term, s));
+  // RoPE, rotation and INT4 append of the new token, rotated queries,
+  // attention over positions 0..cached_lens[b] in splits (one kernel), the
+  // merge of the splits and the inverse rotation (a second kernel unless the
+  // plan has one workgroup per sequence) -> the O projection operand
+  // (FUTX_O_TERMS bf16 terms)
+  if (run(FUTX_STAGE_ATTENTION)) {
+    AttnArgs aa{};
+    aa.qkv = ws.qkv;
+    aa.cached_lens = cached_lens;
+    aa.block_table = block_table;
+    aa.mpps = max_pages_per_seq;
+    aa.nq = nq;
+    aa.hb = d.had_block;
+    aa.tmax = max_context;
+    aa.theta = d.rope_theta;
+    aa.kv = kv;
+    aa.wpart = ws.apart;
+    aa.out_bf16 = ws.act;
+    aa.term_stride = term;
+    STEP(launch_attn_decode(aa, B, D, attn_plan(B, d.n_kv_heads, max_context), s));
+  }
   // O projection + residual: h = x + O(o)
   if (run(FUTX_STAGE_O)) STEP(gemm(w->o, H, nq * D, ws.act, FUTX_O_TERMS, false, kEpiResid, x, ws.h, nullptr));
   // RMSNorm-2 + gate/up + SwiGLU -> bf16 activation
@@ -377,6 +393,8 @@ static futx_status decode_block_impl(const futx_dims* dims, const futx_block_wei
 #undef STEP
   return FUTX_OK;
 }
+
+extern "C" {
 
 futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
                               float* x, const int32_t* cached_lens, const int32_t* block_table,
@@ -431,15 +449,15 @@ futx_status futx_int4_linear(const futx_dims* dims, futx_proj proj, const futx_q
   return FUTX_OK;
 }
 
-futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const uint16_t* q_rot,
-                                  const int32_t* lens, const int32_t* block_table,
+futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const float* qkv,
+                                  const int32_t* cached_lens, const int32_t* block_table,
                                   int32_t max_pages_per_seq, int32_t max_context,
                                   const futx_kv_cache* cache, float* out, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   clear_error();
   futx_status st = check_dims(dims);
   if (st || (st = check_cache(cache))) return st;
-  if (batch < 1 || batch > kMaxBatch || !q_rot || !lens || !block_table || !out || !workspace)
+  if (batch < 1 || batch > kMaxBatch || !qkv || !cached_lens || !block_table || !out || !workspace)
     return fail(FUTX_E_ARG, "decode_attention: bad args");
   if (max_pages_per_seq < 1 || max_context < 1 ||
       (long)max_pages_per_seq * kPageSize < (long)max_context)
@@ -450,13 +468,21 @@ futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const ui
     return fail(FUTX_E_WORKSPACE, "decode_attention: workspace %zu < %zu bytes", workspace_bytes, ws.bytes);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  AttnPlan ap = attn_plan(batch, d.n_kv_heads, max_context);
-  if ((e = launch_attention(q_rot, false, lens, 0, block_table, max_pages_per_seq, batch, d.n_heads,
-                            d.head_dim, ap, kv_cptrs(cache, d.n_kv_heads), ws.apart, s)) != hipSuccess)
-    return hip_fail(e, "attention");
-  if ((e = launch_attn_merge(ws.apart, lens, 0, batch, d.n_heads, d.head_dim, ap, d.had_block, out,
-                             nullptr, 0, s)) != hipSuccess)
-    return hip_fail(e, "merge");
+  AttnArgs aa{};
+  aa.qkv = qkv;
+  aa.cached_lens = cached_lens;
+  aa.block_table = block_table;
+  aa.mpps = max_pages_per_seq;
+  aa.nq = d.n_heads;
+  aa.hb = d.had_block;
+  aa.tmax = max_context;
+  aa.theta = d.rope_theta;
+  aa.kv = kv_ptrs(cache, d.n_kv_heads);
+  aa.wpart = ws.apart;
+  aa.out_f32 = out;
+  if ((e = launch_attn_decode(aa, batch, d.head_dim, attn_plan(batch, d.n_kv_heads, max_context), s)) !=
+      hipSuccess)
+    return hip_fail(e, "decode_attention");
   return FUTX_OK;
 }
 

@@ -35,4 +35,15 @@ futx_status check_proj(futx_proj p);
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace bytes futx_decode_block carves for exactly `batch` sequences and
+// `max_context` (dims already checked).
+size_t decode_workspace_bytes(const futx_dims& d, int batch, int max_context);
+
+// futx_decode_block (stage < 0) or one of its stages, with a given
+// workspace; validates every argument.
+futx_status decode_block_impl(const futx_dims* dims, const futx_block_weights* w, int32_t batch, float* x,
+                              const int32_t* cached_lens, const int32_t* block_table, int32_t max_pages_per_seq,
+                              int32_t max_context, const futx_kv_cache* cache, void* workspace,
+                              size_t workspace_bytes, void* stream, int stage);
+
 }  // namespace futx

@@ -39,17 +39,6 @@ __global__ __launch_bounds__(256) void prep_act_kernel(const float* __restrict__
   if (threadIdx.x == 0) invr[b] = 1.0f / sqrtf(red[0] / (float)H + eps);
 }
 
-// gsum[j * 32 + b] = sum of the bf16 values act[b][j*G .. j*G+G-1], exact in
-// fp64, stored as an fp32 (hi, lo) pair.
-__global__ __launch_bounds__(64) void gsum_kernel(const uint16_t* __restrict__ act, int K, int G,
-                                                  float2* __restrict__ gsum) {
-  const int j = blockIdx.x, b = blockIdx.y;
-  double s = 0.0;
-  for (int c = threadIdx.x; c < G; c += 64) s += (double)bf16_bits_to_f32(act[(size_t)b * K + (size_t)j * G + c]);
-  s = wave_sum_f64(s);
-  if (threadIdx.x == 0) gsum[j * kMaxBatch + b] = split_f64(s);
-}
-
 // ---------------------------------------------------- split-K epilogues
 // (the INT4 GEMM itself is in gemm.hip; with K split it writes fp32 partial
 // sums part[split][b][P] in physical row order, finished here)
@@ -78,14 +67,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 }
 
 // SwiGLU of the gate/up partials: act[b][c] = bf16(silu(g) * u) with
-// g = invr[b] * sum(gate partials), u = invr[b] * sum(up partials); also the
-// bf16 group sums of act for the down projection.  One block of G threads
-// per (group, sequence).
-__global__ __launch_bounds__(128) void swiglu_kernel(const float* __restrict__ part, int S, int B,
-                                                     int I, int G, const float* __restrict__ invr,
-                                                     uint16_t* __restrict__ act,
-                                                     float2* __restrict__ gsum) {
-  const int c = blockIdx.x * G + threadIdx.x, b = blockIdx.y;
+// g = invr[b] * sum(gate partials), u = invr[b] * sum(up partials).
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, int B, int I,
+                                                     const float* __restrict__ invr, uint16_t* __restrict__ act) {
+  const int c = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+  if (c >= I) return;
   const int N = 2 * I;
   const int Pg = 32 * (c >> 4) + (c & 15), Pu = Pg + 16;
   float g = 0.f, u = 0.f;
@@ -95,14 +81,7 @@ __global__ __launch_bounds__(128) void swiglu_kernel(const float* __restrict__ p
   }
   g *= invr[b];
   u *= invr[b];
-  const float a = g / (1.0f + expf(-g)) * u;
-  const uint16_t ab = f32_to_bf16_bits(a);
-  act[(size_t)b * I + c] = ab;
-  const double s = wave_sum_f64((double)bf16_bits_to_f32(ab));
-  __shared__ double red[2];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) gsum[blockIdx.x * kMaxBatch + b] = split_f64(G > 64 ? red[0] + red[1] : red[0]);
+  act[(size_t)b * I + c] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
 }
 
 // ---------------------------------------------------------------- KV append
@@ -125,21 +104,26 @@ __device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, floa
   *c = (float)cs;
 }
 
-// Rotate-half RoPE of one head held as channel c = lane + 64 j.
+// Rotate-half RoPE of one head held as channel c = lane + 64 j, given cos /
+// sin of frequency index lane % (D / 2) (rope_cs).
 template <int D>
-__device__ __forceinline__ void rope_lane(float (&x)[D / 64], int pos, float theta) {
+__device__ __forceinline__ void rope_lane_cs(float (&x)[D / 64], float c, float s) {
   const int lane = threadIdx.x & 63;
-  float c, s;
   if constexpr (D == 128) {
-    rope_cs(pos, lane, D, theta, &c, &s);
     const float a = x[0], b = x[1];
     x[0] = a * c - b * s;
     x[1] = b * c + a * s;
   } else {
-    rope_cs(pos, lane & 31, D, theta, &c, &s);
     const float o = __shfl_xor(x[0], 32, 64);
     x[0] = lane < 32 ? x[0] * c - o * s : x[0] * c + o * s;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void rope_lane(float (&x)[D / 64], int pos, float theta) {
+  float c, s;
+  rope_cs(pos, (threadIdx.x & 63) % (D / 2), D, theta, &c, &s);
+  rope_lane_cs<D>(x, c, s);
 }
 
 // Normalized Sylvester Hadamard over contiguous blocks of hb channels
@@ -178,29 +162,48 @@ __device__ __forceinline__ uint16_t quantize_lane(const float (&x)[D / 64], int 
   return __half_as_ushort(s16);
 }
 
-// Writes one rotated token of KV head h into its slot.
+// One new token of KV head h in registers: the codes of channel
+// c = lane + 64 j (quantize_lane), the packed key word of the lane's run of
+// 8 channels (valid in lanes with lane % 8 == 0, channels lane + 64 j ..
+// lane + 64 j + 7, in the key layout of layout.h) and the fp16 scales.
 template <int D>
-__device__ void store_token(const float (&kx)[D / 64], const float (&vx)[D / 64], int slot, int h,
-                            const KVPtrs& kv) {
-  const int lane = threadIdx.x & 63;
-  const int page = slot / kPageSize, off = slot % kPageSize;
-  const size_t head_base = ((size_t)page * kv.nkv + h) * (size_t)(kPageSize * D / 2);
+struct TokenCodes {
   int qk[D / 64], qv[D / 64];
-  const uint16_t sk = quantize_lane<D>(kx, qk);
-  const uint16_t sv = quantize_lane<D>(vx, qv);
-  // keys: 8 consecutive channels form one word of the lane chunk of token off
-  const int e = lane & 7, g = (lane & 31) >> 3;
+  uint32_t kword[D / 64];
+  uint16_t sk, sv;
+};
+
+template <int D>
+__device__ __forceinline__ void quantize_token(const float (&kx)[D / 64], const float (&vx)[D / 64],
+                                               TokenCodes<D>& t) {
+  const int lane = threadIdx.x & 63, e = lane & 7;
+  t.sk = quantize_lane<D>(kx, t.qk);
+  t.sv = quantize_lane<D>(vx, t.qv);
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) {
-    uint32_t w = nibble_bits(e, (uint32_t)(qk[j] + (int)kNibbleBias));
+    uint32_t w = nibble_bits(e, (uint32_t)(t.qk[j] + (int)kNibbleBias));
     w |= __shfl_xor(w, 1, 64);
     w |= __shfl_xor(w, 2, 64);
     w |= __shfl_xor(w, 4, 64);
+    t.kword[j] = w;
+  }
+}
+
+// Writes one quantized token of KV head h into its slot.
+template <int D>
+__device__ void store_token(const TokenCodes<D>& t, int slot, int h, const KVPtrs& kv) {
+  const int lane = threadIdx.x & 63;
+  const int page = slot / kPageSize, off = slot % kPageSize;
+  const size_t head_base = ((size_t)page * kv.nkv + h) * (size_t)(kPageSize * D / 2);
+  // keys: the word of 8 consecutive channels of token off
+  const int e = lane & 7, g = (lane & 31) >> 3;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
     if (e == 0) {
       const int s = (lane >> 5) + 2 * j;
       uint8_t* p = kv.k_codes + head_base + (size_t)(off >> 4) * (8 * D) +
                    (size_t)(g * 16 + (off & 15)) * (D / 8) + s * 4;
-      *(uint32_t*)p = w;
+      *(uint32_t*)p = t.kword[j];
     }
   }
   // values: one nibble per channel in a word shared with 7 other tokens
@@ -215,11 +218,11 @@ __device__ void store_token(const float (&kx)[D / 64], const float (&vx)[D / 64]
     uint32_t* p = (uint32_t*)(kv.v_codes + head_base + (size_t)(tb * (D / 64) + cg) * 1024 +
                               (size_t)(gv * 16 + (c & 15)) * 16 + c4 * 4);
     atomicAnd(p, ~vmask);
-    atomicOr(p, nibble_bits(ev, (uint32_t)(qv[j] + (int)kNibbleBias)));
+    atomicOr(p, nibble_bits(ev, (uint32_t)(t.qv[j] + (int)kNibbleBias)));
   }
   if (lane == 0) {
-    kv.k_scales[((size_t)page * kv.nkv + h) * kPageSize + off] = sk;
-    kv.v_scales[((size_t)page * kv.nkv + h) * kPageSize + off] = sv;
+    kv.k_scales[((size_t)page * kv.nkv + h) * kPageSize + off] = t.sk;
+    kv.v_scales[((size_t)page * kv.nkv + h) * kPageSize + off] = t.sv;
   }
 }
 
@@ -243,7 +246,9 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const float* __restrict__
     fwht_lane<D>(kx, hb);
     fwht_lane<D>(vx, hb);
   }
-  store_token<D>(kx, vx, slots[t], h, kv);
+  TokenCodes<D> tc;
+  quantize_token<D>(kx, vx, tc);
+  store_token<D>(tc, slots[t], h, kv);
 }
 
 // ---------------------------------------------------------------- attention
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const float* __restrict__
 // Split-sequence decode attention.  One wave per (chunk, KV head, sequence)
 // computes, for the G query heads of the KV head, the chunk's running max m,
 // normalizer l and unnormalized p.v accumulator over rotated INT4 keys and
-// values (flash-decoding partials, merged by attn_merge_kernel).
+// values (flash-decoding partials, merged as attn_decode_kernel describes).
 //   q.k:  A = key tile (16 tokens x 32 channels per MFMA), B = rotated query
 //         (query heads as columns) -> scores[token][head] with the token of
 //         lane L, reg r at 4 (L/16) + r.
@@ -263,7 +268,6 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const float* __restrict__
 // accumulators), and the two fp32 operands (query, p * value scale) enter
 // the fp16 MFMA as a hi + lo pair (22 significant bits) after an exact
 // power-of-two scaling into fp16 range.
-// apart[((b * nq + i) * nsplit + sp) * (D + 2)] = {m, l, acc[0..D)}.
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
@@ -314,141 +318,185 @@ __device__ __forceinline__ float q_fragments(const float (&qv)[D / 32][8], f16x8
   return ldexpf(1.0f, -kq);
 }
 
+// A 32-token block of one page and KV head in the attention operand layout
+// (layout.h): key words of its two 16-token tiles, value words of its
+// channel groups, and the fp16 scales of the tokens 4 grp + r of each tile.
+template <int D>
+struct KvBlk {
+  uint32_t kw[2][D / 32];
+  uint4 vw[D / 64];
+  uint2 k2[2], v2[2];
+};
+
+template <int D>
+__device__ __forceinline__ void load_blk(const KVPtrsConst& kv, int page, int off, int h, KvBlk<D>& r) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  const size_t hb_off = ((size_t)page * kv.nkv + h) * ((size_t)kPageSize * D / 2);
+  const size_t sc_off = ((size_t)page * kv.nkv + h) * kPageSize + off;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint8_t* p = kv.k_codes + hb_off + (size_t)((off >> 4) + u) * (8 * D) + (size_t)lane * (D / 8);
+    if constexpr (D == 128) {
+      const uint4 v = *(const uint4*)p;
+      r.kw[u][0] = v.x; r.kw[u][1] = v.y; r.kw[u][2] = v.z; r.kw[u][3] = v.w;
+    } else {
+      const uint2 v = *(const uint2*)p;
+      r.kw[u][0] = v.x; r.kw[u][1] = v.y;
+    }
+  }
+#pragma unroll
+  for (int cg = 0; cg < D / 64; ++cg)
+    r.vw[cg] = *(const uint4*)(kv.v_codes + hb_off + (size_t)((off >> 5) * (D / 64) + cg) * 1024 + (size_t)lane * 16);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    r.k2[u] = *(const uint2*)(kv.k_scales + sc_off + 16 * u + 4 * grp);
+    r.v2[u] = *(const uint2*)(kv.v_scales + sc_off + 16 * u + 4 * grp);
+  }
+}
+
+// The new token as a block whose token 0 it is (tokens 1..31 are masked by
+// the caller's length).  Key word s of lane L (token L % 16, channels
+// 32 s + 8 (L / 16) + e) is the packed word of lane 8 (L / 16) + 32 (s % 2),
+// run s / 2; value word c4 of channel group cg holds the code of channel
+// cg * 64 + 16 c4 + L % 16 in element 0 (token 0) and code 0 elsewhere.
+// The codes are the ones written to the cache, so the token enters exactly
+// as it would when read back.
+template <int D>
+__device__ __forceinline__ void token_blk(const TokenCodes<D>& t, KvBlk<D>& r) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    const uint32_t w = __shfl(t.kword[s >> 1], 8 * grp + 32 * (s & 1), 64);
+    r.kw[0][s] = w;
+    r.kw[1][s] = w;
+  }
+  uint32_t zero_codes = 0;
+#pragma unroll
+  for (int e = 1; e < 8; ++e) zero_codes |= nibble_bits(e, kNibbleBias);
+#pragma unroll
+  for (int cg = 0; cg < D / 64; ++cg) {
+    uint32_t w4[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int code = __shfl(t.qv[cg], 16 * c4 + (lane & 15), 64);
+      w4[c4] = zero_codes | nibble_bits(0, (uint32_t)(code + (int)kNibbleBias));
+    }
+    r.vw[cg] = uint4{w4[0], w4[1], w4[2], w4[3]};
+  }
+  r.k2[0] = uint2{(uint32_t)t.sk, 0u};
+  r.k2[1] = uint2{0u, 0u};
+  r.v2[0] = uint2{(uint32_t)t.sv, 0u};
+  r.v2[1] = uint2{0u, 0u};
+}
+
+// Online-softmax update with one 32-token block starting at token blk
+// (tokens >= t1 masked; at least one token of the block must be < t1):
+// running max m_i and normalizer part l_part of query head col (per lane),
+// p.v accumulators acc (row 4 grp + r = head, column = channel).
+template <int D>
+__device__ __forceinline__ void compute_blk(int blk, int t1, const KvBlk<D>& rb, const f16x8 (&qh)[D / 32],
+                                            const f16x8 (&ql)[D / 32], float zscale, float& m_i, float& l_part,
+                                            f32x4 (&acc)[D / 16]) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  float ks[2][4], vs[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint2 k2 = rb.k2[u], v2 = rb.v2[u];
+    ks[u][0] = half_bits_to_f32(k2.x & 0xFFFF); ks[u][1] = half_bits_to_f32(k2.x >> 16);
+    ks[u][2] = half_bits_to_f32(k2.y & 0xFFFF); ks[u][3] = half_bits_to_f32(k2.y >> 16);
+    vs[u][0] = half_bits_to_f32(v2.x & 0xFFFF); vs[u][1] = half_bits_to_f32(v2.x >> 16);
+    vs[u][2] = half_bits_to_f32(v2.y & 0xFFFF); vs[u][3] = half_bits_to_f32(v2.y >> 16);
+  }
+  // scores
+  float z[2][4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const f16x8 kc = widen_word_exact_f16(rb.kw[u][s]);
+      d = mfma16h(kc, qh[s], d);
+      d = mfma16h(kc, ql[s], d);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = blk + 16 * u + 4 * grp + r;
+      z[u][r] = t < t1 ? d[r] * ks[u][r] * zscale : -INFINITY;
+      if (t >= t1) vs[u][r] = 0.f;  // stale scales past the end stay out of p.v
+      mloc = fmaxf(mloc, z[u][r]);
+    }
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+  const float m_new = fmaxf(m_i, mloc);
+  const float alpha = expf(m_i - m_new);
+  // exact power-of-two scaling of p * vs (<= max vs) into fp16 range
+  float vmax = fmaxf(fmaxf(fmaxf(vs[0][0], vs[0][1]), fmaxf(vs[0][2], vs[0][3])),
+                     fmaxf(fmaxf(vs[1][0], vs[1][1]), fmaxf(vs[1][2], vs[1][3])));
+  vmax = fmaxf(vmax, __shfl_xor(vmax, 16, 64));
+  vmax = fmaxf(vmax, __shfl_xor(vmax, 32, 64));
+  const int kp = range_exp(vmax, 14);
+  float psum = 0.f;
+  uint32_t phw[4], plw[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {
+      const float p0 = expf(z[u][r] - m_new), p1 = expf(z[u][r + 1] - m_new);
+      psum += p0 + p1;
+      _Float16 h0, l0, h1, l1;
+      split_f16(ldexpf(p0 * vs[u][r], kp), &h0, &l0);
+      split_f16(ldexpf(p1 * vs[u][r + 1], kp), &h1, &l1);
+      phw[2 * u + r / 2] = pack_h2(h0, h1);
+      plw[2 * u + r / 2] = pack_h2(l0, l1);
+    }
+  }
+  l_part = l_part * alpha + psum;
+  m_i = m_new;
+  const f16x8 pah = __builtin_bit_cast(f16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
+  const f16x8 pal = __builtin_bit_cast(f16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
+  // rescale the p.v accumulators: row 4 (L/16) + r belongs to head 4 grp + r
+  float al[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
+  const float pback = ldexpf(1.0f, -kp);
+#pragma unroll
+  for (int cg = 0; cg < D / 64; ++cg)
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const f16x8 vc = widen_word_exact_f16(word_of(rb.vw[cg], c4));
+      f32x4 dv = mfma16h(pah, vc, f32x4{0.f, 0.f, 0.f, 0.f});
+      dv = mfma16h(pal, vc, dv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
+    }
+}
+
 // Online-softmax scan of tokens [t0, t1) of one sequence (block table row
-// bt) against KV head h, for the query heads of the fragments: running max
-// m_i and normalizer part l_part of head col (per lane), and the p.v
-// accumulators acc (row 4 grp + r = head, column = channel).  make_q() runs
-// once, after the first page's loads are issued and before its scores, and
-// may fill the fragments and zscale (their latency then overlaps).
+// bt, t0 page-aligned) against KV head h.  make_q() runs once, after the
+// first page's loads are issued and before its scores, and may fill the
+// query fragments and zscale (their latency then overlaps).  Pages are
+// double-buffered: the loads of page i + 1 are issued before page i is
+// computed; past the last page the loads repeat it (valid addresses) and
+// are not used.
 template <int D, typename MakeQ>
 __device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x8 (&ql)[D / 32],
                                            const float& zscale, const int32_t* bt, int t0, int t1, int h,
-                                           const KVPtrsConst& kv, float& m_i, float& l_part,
+                                           int page0, const KVPtrsConst& kv, float& m_i, float& l_part,
                                            f32x4 (&acc)[D / 16], MakeQ&& make_q) {
-  const int lane = threadIdx.x & 63, grp = lane >> 4;
-  const int nkv = kv.nkv;
-  const size_t head_bytes = (size_t)kPageSize * D / 2;
-  // One 64-token page per iteration: the codes and scales of its two
-  // 32-token blocks are loaded together, and the next page's table entry one
-  // page ahead, so no load waits on a page index just loaded.
-  struct Blk {
-    uint32_t kw[2][D / 32];
-    uint4 vw[D / 64];
-    uint2 k2[2], v2[2];
+  auto issue_page = [&](int pg, KvBlk<D>& r0, KvBlk<D>& r1) {
+    load_blk<D>(kv, pg, 0, h, r0);
+    load_blk<D>(kv, pg, 32, h, r1);
   };
-  auto load_blk = [&](int page, int off, Blk& r) {
-    const size_t hb_off = ((size_t)page * nkv + h) * head_bytes;
-    const size_t sc_off = ((size_t)page * nkv + h) * kPageSize + off;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint8_t* p = kv.k_codes + hb_off + (size_t)((off >> 4) + u) * (8 * D) + (size_t)lane * (D / 8);
-      if constexpr (D == 128) {
-        const uint4 v = *(const uint4*)p;
-        r.kw[u][0] = v.x; r.kw[u][1] = v.y; r.kw[u][2] = v.z; r.kw[u][3] = v.w;
-      } else {
-        const uint2 v = *(const uint2*)p;
-        r.kw[u][0] = v.x; r.kw[u][1] = v.y;
-      }
-    }
-#pragma unroll
-    for (int cg = 0; cg < D / 64; ++cg)
-      r.vw[cg] = *(const uint4*)(kv.v_codes + hb_off + (size_t)((off >> 5) * (D / 64) + cg) * 1024 + (size_t)lane * 16);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      r.k2[u] = *(const uint2*)(kv.k_scales + sc_off + 16 * u + 4 * grp);
-      r.v2[u] = *(const uint2*)(kv.v_scales + sc_off + 16 * u + 4 * grp);
-    }
+  auto issue = [&](int pt, KvBlk<D>& r0, KvBlk<D>& r1) { issue_page(bt[min(pt, t1 - 1) / kPageSize], r0, r1); };
+  auto consume = [&](int pt, const KvBlk<D>& r0, const KvBlk<D>& r1) {
+    compute_blk<D>(pt, t1, r0, qh, ql, zscale, m_i, l_part, acc);
+    if (pt + 32 < t1) compute_blk<D>(pt + 32, t1, r1, qh, ql, zscale, m_i, l_part, acc);
   };
-  auto compute_blk = [&](int blk, const Blk& rb) {
-    float ks[2][4], vs[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint2 k2 = rb.k2[u], v2 = rb.v2[u];
-      ks[u][0] = half_bits_to_f32(k2.x & 0xFFFF); ks[u][1] = half_bits_to_f32(k2.x >> 16);
-      ks[u][2] = half_bits_to_f32(k2.y & 0xFFFF); ks[u][3] = half_bits_to_f32(k2.y >> 16);
-      vs[u][0] = half_bits_to_f32(v2.x & 0xFFFF); vs[u][1] = half_bits_to_f32(v2.x >> 16);
-      vs[u][2] = half_bits_to_f32(v2.y & 0xFFFF); vs[u][3] = half_bits_to_f32(v2.y >> 16);
-    }
-    // scores
-    float z[2][4];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        const f16x8 kc = widen_word_exact_f16(rb.kw[u][s]);
-        d = mfma16h(kc, qh[s], d);
-        d = mfma16h(kc, ql[s], d);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = blk + 16 * u + 4 * grp + r;
-        z[u][r] = t < t1 ? d[r] * ks[u][r] * zscale : -INFINITY;
-        if (t >= t1) vs[u][r] = 0.f;  // stale scales past the end stay out of p.v
-        mloc = fmaxf(mloc, z[u][r]);
-      }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_i, mloc);
-    const float alpha = expf(m_i - m_new);
-    // exact power-of-two scaling of p * vs (<= max vs) into fp16 range
-    float vmax = fmaxf(fmaxf(fmaxf(vs[0][0], vs[0][1]), fmaxf(vs[0][2], vs[0][3])),
-                       fmaxf(fmaxf(vs[1][0], vs[1][1]), fmaxf(vs[1][2], vs[1][3])));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 16, 64));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 32, 64));
-    const int kp = range_exp(vmax, 14);
-    float psum = 0.f;
-    uint32_t phw[4], plw[4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const float p0 = expf(z[u][r] - m_new), p1 = expf(z[u][r + 1] - m_new);
-        psum += p0 + p1;
-        _Float16 h0, l0, h1, l1;
-        split_f16(ldexpf(p0 * vs[u][r], kp), &h0, &l0);
-        split_f16(ldexpf(p1 * vs[u][r + 1], kp), &h1, &l1);
-        phw[2 * u + r / 2] = pack_h2(h0, h1);
-        plw[2 * u + r / 2] = pack_h2(l0, l1);
-      }
-    }
-    l_part = l_part * alpha + psum;
-    m_i = m_new;
-    const f16x8 pah = __builtin_bit_cast(f16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
-    const f16x8 pal = __builtin_bit_cast(f16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
-    // rescale the p.v accumulators: row 4 (L/16) + r belongs to head 4 grp + r
-    float al[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
-    const float pback = ldexpf(1.0f, -kp);
-#pragma unroll
-    for (int cg = 0; cg < D / 64; ++cg)
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const f16x8 vc = widen_word_exact_f16(word_of(rb.vw[cg], c4));
-        f32x4 dv = mfma16h(pah, vc, f32x4{0.f, 0.f, 0.f, 0.f});
-        dv = mfma16h(pal, vc, dv);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
-      }
-  };
-  // Pages are double-buffered: the loads of page i + 1 are issued before
-  // page i is computed (t0 is page-aligned: splits are whole pages).  Past
-  // the last page the loads repeat it (valid addresses) and are not used.
-  auto issue = [&](int pt, Blk& r0, Blk& r1) {
-    const int pg = bt[min(pt, t1 - 1) / kPageSize];
-    load_blk(pg, 0, r0);
-    load_blk(pg, 32, r1);
-  };
-  auto consume = [&](int pt, const Blk& r0, const Blk& r1) {
-    compute_blk(pt, r0);
-    if (pt + 32 < t1) compute_blk(pt + 32, r1);
-  };
-  Blk a0, a1, b0, b1;
+  KvBlk<D> a0, a1, b0, b1;
   int pt = t0;
-  issue(pt, a0, a1);
+  issue_page(page0, a0, a1);  // the first page's table entry was read by the caller (bt[t0 / page size])
   make_q();  // the query work overlaps the first page's loads
   for (;;) {
     issue(pt + kPageSize, b0, b1);
@@ -459,77 +507,6 @@ __device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x
     consume(pt, b0, b1);
     pt += kPageSize;
     if (pt >= t1) break;
-  }
-}
-
-template <int D, bool QF32>
-__global__ __launch_bounds__(64) void attn_split_kernel(
-    const void* __restrict__ qin, const int32_t* __restrict__ lens, int len_add,
-    const int32_t* __restrict__ block_table, int mpps, int nq, int chunk, int nsplit, float scale,
-    KVPtrsConst kv, float* __restrict__ apart) {
-  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const int nkv = kv.nkv, G = nq / nkv;
-  const int L = lens[b] + len_add;
-  const int t0 = sp * chunk, t1 = min(t0 + chunk, L);
-  if (t0 >= t1) return;
-  const int col = lane & 15, grp = lane >> 4;
-  // query fragments (B operand): column = query head h*G + col
-  f16x8 qh[D / 32], ql[D / 32];
-  float qscale;  // 2^-kq of this lane's head
-  {
-    const bool ok = col < G;
-    const size_t qoff = ((size_t)b * nq + h * G + col) * D;
-    float qv[D / 32][8];
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[s][e] = 0.f;
-      if (ok) {
-        if constexpr (QF32) {
-          const float4* qp = (const float4*)((const float*)qin + qoff + s * 32 + grp * 8);
-          const float4 a = qp[0], c = qp[1];
-          qv[s][0] = a.x; qv[s][1] = a.y; qv[s][2] = a.z; qv[s][3] = a.w;
-          qv[s][4] = c.x; qv[s][5] = c.y; qv[s][6] = c.z; qv[s][7] = c.w;
-        } else {
-          const uint4 v = *(const uint4*)((const uint16_t*)qin + qoff + s * 32 + grp * 8);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qv[s][2 * e] = bf16_bits_to_f32(w[e] & 0xFFFF);
-            qv[s][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
-          }
-        }
-      }
-    }
-    qscale = q_fragments<D>(qv, qh, ql);
-  }
-  float m_i = -INFINITY, l_part = 0.f;
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float zscale = qscale * scale;
-  split_scan<D>(qh, ql, zscale, block_table + (size_t)b * mpps, t0, t1, h, kv, m_i, l_part, acc, [] {});
-  // finalize this chunk's partials
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  float* out = apart + (((size_t)b * nq + h * G) * nsplit + sp) * (D + 2);
-  const size_t head_stride = (size_t)nsplit * (D + 2);
-  if (grp == 0 && col < G) {
-    out[col * head_stride + 0] = m_i;
-    out[col * head_stride + 1] = l_tot;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * grp + r;
-    if (i < G) {
-#pragma unroll
-      for (int cg = 0; cg < D / 64; ++cg)
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const int c = cg * 64 + c4 * 16 + col;
-          out[i * head_stride + 2 + c] = acc[cg * 4 + c4][r];
-        }
-    }
   }
 }
 
@@ -576,74 +553,91 @@ __device__ __forceinline__ void store_terms(float o, uint16_t* out, size_t at, s
   }
 }
 
-// The attention part of the decode block after the QKV projection, up to
-// the cross-workgroup merge (attn_merge_kernel, with 4 * chunk tokens per
-// partial):
-//   * the new token: RoPE of k at position L_b, block rotation of k and v,
-//     per-token INT4 quantization, write to the paged cache at slot L_b;
+// o (fp32) of query head channel c, held in lane c % 64 of a wave whose 64
+// lanes hold 64 consecutive channels: the inverse block rotation (the
+// normalized Sylvester matrix is its own inverse), then the output at
+// element `at` (fp32, and / or FUTX_O_TERMS bf16 terms for the O projection).
+__device__ __forceinline__ void emit_output(float o, int hb, const AttnArgs& a, size_t at) {
+  const int lane = threadIdx.x & 63;
+  for (int hop = 1; hop < hb; hop <<= 1) {
+    const float p = __shfl_xor(o, hop, 64);
+    o = (lane & hop) ? p - o : o + p;
+  }
+  o *= 1.0f / sqrtf((float)hb);
+  if (a.out_f32) a.out_f32[at] = o;
+  if (a.out_bf16) store_terms<FUTX_O_TERMS>(o, a.out_bf16, at, a.term_stride);
+}
+
+// The attention part of the decode block after the QKV projection.  Grid
+// (workgroups per sequence, KV heads, sequences); each of the 4 waves of a
+// workgroup owns one split of `chunk` tokens:
+//   * the wave whose split holds the new token (position L_b) applies RoPE
+//     to its key, the block rotation to its key and value, quantizes both
+//     per token and writes them to the paged cache at slot L_b; the token's
+//     score and value enter the softmax from those same codes in registers
+//     (token_blk), so nothing waits on the cache write;
 //   * the rotated queries (RoPE + block rotation) of the G query heads of
-//     the KV head, recomputed by every wave from the fp32 projection;
-//   * split-sequence attention over positions 0..L_b (the new token read
-//     back from the cache), four splits per workgroup (one per wave),
-//     merged in LDS into one partial (m, l, acc) per workgroup and head.
+//     the KV head are recomputed by every wave from the fp32 projection;
+//   * split-sequence attention over the cached tokens, the four splits of a
+//     workgroup merged in LDS into one partial (m, l, acc) per head, which
+//     attn_merge_kernel combines across workgroups; when the plan has one
+//     workgroup per sequence, the output (inverse rotation included) is
+//     written here and no merge runs.
+// (Publishing the partials to the last workgroup to arrive, through
+// agent-scope coherent stores and an arrival counter, measured slower on
+// MI355X than the separate merge launch: 15.1 us against 9.6 + 3.1 us at
+// 8B batch 1.)
 // Steps from the FuTransformer pages: K/V rotated by a block Hadamard before
 // INT4 caching and the rotation undone on the output (kongchang.com/en,
 // section "INT4 Decode: letting dequantization feed directly into MMA
 // operands"); results written straight into cache locations (same article,
 // section "FP8 Prefill: fusing GEMM and epilogue all the way").
-// wpart[((b * nq + i) * nwg + w) * (D + 2)] = {m, l, acc[0..D)} of workgroup w.
-// (A merge in this kernel by the last workgroup to finish needs device-scope
-// fences around a counter; on this chip each one writes back the L2, and
-// that cost more than the separate merge launch.)
+// A cached length outside the plan (L_b < 0 or L_b + 1 > tmax) writes
+// nothing here (the merge, or this kernel when it finishes, makes that
+// group's output NaN).
+// (two workgroups per CU: the register budget stays at 256 per lane)
 template <int D>
-__global__ __launch_bounds__(256) void attn_decode_kernel(
-    const float* __restrict__ qkv, int nq, const int32_t* __restrict__ cached_lens,
-    const int32_t* __restrict__ block_table, int mpps, int chunk, int nwg, int hb, float theta, float scale,
-    KVPtrs kv, float* __restrict__ wpart) {
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   constexpr int MAXG = 16;  // query heads per KV head (matrix-core columns)
   __shared__ float s_m[4][MAXG], s_l[4][MAXG];
   __shared__ float s_acc[4][MAXG][D];
   const int wg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int col = lane & 15, grp = lane >> 4;
-  const int nkv = kv.nkv, G = nq / nkv;
-  const int pos = cached_lens[b];  // the new token's position
-  const int T = pos + 1;           // tokens attended to
-  const int nsp = (T + chunk - 1) / chunk;
+  const int nkv = a.kv.nkv, G = a.nq / nkv;
+  // the table entry of this wave's first page does not depend on the
+  // sequence length: its load goes out together with the length's
+  const int sp = wg * 4 + wv;
+  const int t0 = sp * a.chunk;
+  const int32_t* const bt = a.block_table + (size_t)b * a.mpps;
+  const int page0 = bt[min(t0 / kPageSize, a.mpps - 1)];
+  const int pos = a.cached_lens[b];  // the new token's position
+  const int T = pos + 1;             // tokens attended to
+  const size_t obase = ((size_t)b * a.nq + (size_t)h * G) * D;  // output of the group's first head
+  if (pos < 0 || T > a.tmax) {
+    if (wg == 0 && a.nwg == 1) {
+      for (int p = tid; p < G * D; p += 256) {
+        if (a.out_f32) a.out_f32[obase + p] = __builtin_nanf("");
+        if (a.out_bf16)
+#pragma unroll
+          for (int t = 0; t < FUTX_O_TERMS; ++t) a.out_bf16[obase + p + t * a.term_stride] = 0x7FC0;
+      }
+    }
+    return;
+  }
+  const int nsp = (T + a.chunk - 1) / a.chunk;
   const int nwg_b = (nsp + 3) / 4;
   if (wg >= nwg_b) return;  // the whole workgroup, before any barrier
-  const float* row = qkv + (size_t)b * (nq + 2 * nkv) * D;
-  const KVPtrsConst kvc{kv.k_codes, kv.v_codes, kv.k_scales, kv.v_scales, nkv};
+  const float* row = a.qkv + (size_t)b * (a.nq + 2 * nkv) * D;
+  const KVPtrsConst kvc{a.kv.k_codes, a.kv.v_codes, a.kv.k_scales, a.kv.v_scales, nkv};
+  const int t1 = min(t0 + a.chunk, T);
+  const bool owner = sp == pos / a.chunk;  // wave-uniform
+  const int t1s = owner ? pos : t1;        // cached tokens of the split (the new one comes from registers)
 
-  // 1. the new token's key and value, by the wave of the last split (the
-  //    only wave that reads the token's page), before its scan
-  if (wg * 4 + wv == nsp - 1) {
-    float kx[D / 64], vx[D / 64];
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-      kx[j] = row[(nq + h) * D + lane + 64 * j];
-      vx[j] = row[(nq + nkv + h) * D + lane + 64 * j];
-    }
-    rope_lane<D>(kx, pos, theta);
-    fwht_lane<D>(kx, hb);
-    fwht_lane<D>(vx, hb);
-    const int slot = block_table[(size_t)b * mpps + pos / kPageSize] * kPageSize + pos % kPageSize;
-    store_token<D>(kx, vx, slot, h, kv);
-    // The scan below reads the token back; only this wave reads its page.
-    // One wave's memory operations reach the (write-through) L1 and the L2
-    // in program order, so its later loads see these stores and atomics; the
-    // workgroup-scope fence only keeps the compiler from reordering them.
-    // (A device-scope fence would write back the whole L2, which costs
-    // microseconds per call on this chip.)
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  }
-
-  // 2. rotated queries of the group's heads, as matrix-core fragments
-  //    (computed inside the scan, while the first page's loads are in flight)
-  //    The query loads go out first (loads complete in order, so the KV
-  //    loads issued after them stay in flight while the queries are used).
-  f16x8 qh[D / 32], ql[D / 32];
-  float zscale = 0.f;
+  // 1. loads: the group's queries and the new token's key and value (every
+  //    wave loads them, only the owner uses the key and value: unconditional
+  //    loads keep the memory-counter waits exact)
   const bool ok = col < G;
   float qv[D / 32][8];
   {
@@ -651,14 +645,33 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       const float4* qp = (const float4*)(qrow + s * 32 + grp * 8);
-      const float4 a = qp[0], c = qp[1];
-      qv[s][0] = a.x; qv[s][1] = a.y; qv[s][2] = a.z; qv[s][3] = a.w;
-      qv[s][4] = c.x; qv[s][5] = c.y; qv[s][6] = c.z; qv[s][7] = c.w;
+      const float4 x0 = qp[0], x1 = qp[1];
+      qv[s][0] = x0.x; qv[s][1] = x0.y; qv[s][2] = x0.z; qv[s][3] = x0.w;
+      qv[s][4] = x1.x; qv[s][5] = x1.y; qv[s][6] = x1.z; qv[s][7] = x1.w;
     }
   }
+  float kx[D / 64], vx[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    kx[j] = row[(a.nq + h) * D + lane + 64 * j];
+    vx[j] = row[(a.nq + nkv + h) * D + lane + 64 * j];
+  }
+
+  // 2. rotated queries as matrix-core fragments, and the owner's new-token
+  //    codes (computed inside the scan while the first page's loads are in
+  //    flight)
+  f16x8 qh[D / 32], ql[D / 32];
+  float zscale = 0.f;
+  TokenCodes<D> tok;
   auto make_q = [&]() {
-    float cs, sn;  // cos / sin of frequency index lane % (D / 2)
-    rope_cs(pos, lane % (D / 2), D, theta, &cs, &sn);
+    float cs, sn;  // cos / sin of frequency index lane % (D / 2), shared by the key and the queries
+    rope_cs(pos, lane % (D / 2), D, a.theta, &cs, &sn);
+    if (owner) {
+      rope_lane_cs<D>(kx, cs, sn);
+      fwht_lane<D>(kx, a.hb);
+      fwht_lane<D>(vx, a.hb);
+      quantize_token<D>(kx, vx, tok);
+    }
     // rotate-half RoPE: channel c < D/2 (word s) pairs with c + D/2 (word s + D/64)
 #pragma unroll
     for (int s = 0; s < D / 64; ++s)
@@ -673,28 +686,37 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     // block Hadamard over channel bits: 0..2 in e, 3..4 in grp (lanes 16
     // and 32 apart), 5 in the word index s; one call per hop, so every
     // register index is a compile-time constant
-    if (hb > 1) q_hop<D, 1>(qv, lane);
-    if (hb > 2) q_hop<D, 2>(qv, lane);
-    if (hb > 4) q_hop<D, 4>(qv, lane);
-    if (hb > 8) q_hop<D, 8>(qv, lane);
-    if (hb > 16) q_hop<D, 16>(qv, lane);
-    if (hb > 32) q_hop<D, 32>(qv, lane);
-    const float hsc = 1.0f / sqrtf((float)hb);
+    if (a.hb > 1) q_hop<D, 1>(qv, lane);
+    if (a.hb > 2) q_hop<D, 2>(qv, lane);
+    if (a.hb > 4) q_hop<D, 4>(qv, lane);
+    if (a.hb > 8) q_hop<D, 8>(qv, lane);
+    if (a.hb > 16) q_hop<D, 16>(qv, lane);
+    if (a.hb > 32) q_hop<D, 32>(qv, lane);
+    const float hsc = 1.0f / sqrtf((float)a.hb);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[s][e] = ok ? qv[s][e] * hsc : 0.f;
-    zscale = q_fragments<D>(qv, qh, ql) * scale;
+    zscale = q_fragments<D>(qv, qh, ql) * a.scale;
   };
 
-  // 3. this wave's split
-  const int t0 = (wg * 4 + wv) * chunk, t1 = min(t0 + chunk, T);
+  // 3. this wave's split: the cached tokens, then (owner) the new token
   float m_i = -INFINITY, l_part = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (t0 < t1)
-    split_scan<D>(qh, ql, zscale, block_table + (size_t)b * mpps, t0, t1, h, kvc, m_i, l_part, acc, make_q);
+  if (t0 < t1s)
+    split_scan<D>(qh, ql, zscale, bt, t0, t1s, h, page0, kvc, m_i, l_part, acc, make_q);
+  else if (owner)
+    make_q();
+  if (owner) {
+    KvBlk<D> nb;
+    token_blk<D>(tok, nb);
+    compute_blk<D>(pos, T, nb, qh, ql, zscale, m_i, l_part, acc);
+    // the cache write goes out last: no later load of this wave waits for it
+    const int slot = bt[pos / kPageSize] * kPageSize + pos % kPageSize;
+    store_token<D>(tok, slot, h, a.kv);
+  }
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
 
@@ -714,21 +736,38 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     }
   }
   __syncthreads();
-  const size_t hstride = (size_t)nwg * (D + 2);  // between query heads in wpart
-  float* wp = wpart + (((size_t)b * nq + h * G) * nwg + wg) * (D + 2);
-  for (int p = tid; p < G * D; p += 256) {
-    const int i = p / D, c = p % D;
-    float M = -INFINITY;
+  // (p = i * D + c: D is a multiple of 64 and the stride 256, so the 64
+  //  lanes of a wave always hold 64 consecutive channels of one head)
+  auto lds_partial = [&](int i, int c, float& M, float& l, float& acc_c) {
+    M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][i]);
-    float l = 0.f, a = 0.f;
+    l = 0.f;
+    acc_c = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // a wave with no tokens has m = -inf: weight 0
       const float wt = s_m[w][i] == -INFINITY ? 0.f : expf(s_m[w][i] - M);
       l = fmaf(wt, s_l[w][i], l);
-      a = fmaf(wt, s_acc[w][i][c], a);
+      acc_c = fmaf(wt, s_acc[w][i][c], acc_c);
     }
-    wp[i * hstride + 2 + c] = a;
+  };
+  if (a.nwg == 1) {  // one workgroup per sequence: the output is complete here
+    for (int p = tid; p < G * D; p += 256) {
+      const int i = p / D, c = p % D;
+      float M, l, ac;
+      lds_partial(i, c, M, l, ac);
+      emit_output(l > 0.f ? ac / l : 0.f, a.hb, a, obase + p);
+    }
+    return;
+  }
+  // 5. this workgroup's partial, combined across workgroups by attn_merge_kernel
+  const size_t hstride = (size_t)a.nwg * (D + 2);  // between query heads in wpart
+  float* const wp = a.wpart + (((size_t)b * a.nq + h * G) * a.nwg + wg) * (D + 2);
+  for (int p = tid; p < G * D; p += 256) {
+    const int i = p / D, c = p % D;
+    float M, l, ac;
+    lds_partial(i, c, M, l, ac);
+    wp[i * hstride + 2 + c] = ac;
     if (c == 0) {
       wp[i * hstride] = M;
       wp[i * hstride + 1] = l;
@@ -736,46 +775,56 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 }
 
-// Merge of the split partials + inverse block Hadamard.  One block of 256
-// threads per (query head, sequence).  Writes fp32 output, or the operand of
-// the O projection: o as an unevaluated sum of FUTX_O_TERMS bf16 terms
-// (term t at out_bf16 + t * term_stride).  The attention output comes out of
-// a long fp32 reduction, so a single bf16 rounding here would flip on tiny
-// differences; the terms carry it far below bf16's rounding (gemm.h).
-// Thread t owns channel chunk t % (D/4) (four channels) of the splits
+// Merge of the workgroup partials + inverse block Hadamard.  One block of
+// 256 threads per (query head, sequence).  Writes fp32 output, or the
+// operand of the O projection: o as an unevaluated sum of FUTX_O_TERMS bf16
+// terms (term t at out_bf16 + t * term_stride).  The attention output comes
+// out of a long fp32 reduction, so a single bf16 rounding here would flip on
+// tiny differences; the terms carry it far below bf16's rounding (gemm.h).
+// Thread t owns channel chunk t % (D/4) (four channels) of the partials
 // sp = t / (D/4) + (256 / (D/4)) u.  The partials were written by the
-// previous kernel on other CUs, so every load of a round (U splits per
+// previous kernel on other CUs, so every load of a round (U partials per
 // thread) is issued before any is used, and before the sequence length is
-// known (indices clamped to the workspace's splits, the extra ones masked
-// out afterwards): one round trip per 256 / (D/4) * U splits.
+// known (indices clamped to the workspace's partials, the extra ones masked
+// out afterwards): one round trip per 256 / (D/4) * U partials.  `chunk` is
+// the tokens per partial (four attention splits).  A length outside the plan
+// (lens[b] < 0 or lens[b] + 1 > tmax) gives a NaN output.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(
-    const float* __restrict__ apart, const int32_t* __restrict__ lens, int len_add, int nq,
-    int chunk, int nsplit, int hb, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
-    size_t term_stride) {
-  constexpr int NC = D / 4;     // float4 chunks per split
-  constexpr int PH = 256 / NC;  // split phases
-  constexpr int U = 4;          // splits per thread and round
+    const float* __restrict__ apart, const int32_t* __restrict__ lens, int nq, int chunk, int nsplit,
+    int hb, int tmax, float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16, size_t term_stride) {
+  constexpr int NC = D / 4;     // float4 chunks per partial
+  constexpr int PH = 256 / NC;  // partial phases
+  constexpr int U = 4;          // partials per thread and round
   __shared__ float s_m[PH], s_l[PH];
   __shared__ float4 s_acc[PH][NC];
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63;
   const int ch = t % NC, ph = t / NC;
   const float* base = apart + ((size_t)b * nq + i) * nsplit * (D + 2);
-  const int L = lens[b] + len_add;
+  const int L = lens[b] + 1;  // tokens attended to
+  if (L < 1 || L > tmax) {
+    if (t < D) {
+      const size_t at = ((size_t)b * nq + i) * D + t;
+      if (out_f32) out_f32[at] = __builtin_nanf("");
+      if (out_bf16)
+#pragma unroll
+        for (int k = 0; k < FUTX_O_TERMS; ++k) out_bf16[at + k * term_stride] = 0x7FC0;
+    }
+    return;
+  }
   float m = -INFINITY, l = 0.f;
   float4 a = {0.f, 0.f, 0.f, 0.f};
-  int nsp = nsplit;  // known after the first round's loads are issued
+  const int nsp = min((L + chunk - 1) / chunk, nsplit);
   for (int r0 = 0; r0 < nsp; r0 += PH * U) {
     float mv[U], lv[U];
     float4 av[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float* pw = base + (size_t)min(r0 + ph + PH * u, nsplit - 1) * (D + 2);
+      const float* pw = base + (size_t)min(r0 + ph + PH * u, nsp - 1) * (D + 2);
       mv[u] = pw[0];
       lv[u] = pw[1];
       av[u] = *(const float4*)(pw + 2 + 4 * ch);
     }
-    nsp = min((L + chunk - 1) / chunk, nsplit);
     bool ok[U];
     float mr = m;
 #pragma unroll
@@ -783,7 +832,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
       ok[u] = r0 + ph + PH * u < nsp;
       if (ok[u]) mr = fmaxf(mr, mv[u]);
     }
-    if (mr == -INFINITY) continue;  // no split of this phase in the round
+    if (mr == -INFINITY) continue;  // no partial of this phase in the round
     const float sc = m == -INFINITY ? 0.f : expf(m - mr);
     l *= sc;
     a.x *= sc; a.y *= sc; a.z *= sc; a.w *= sc;
@@ -808,7 +857,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   __syncthreads();
   if (t >= D) return;
   // channel c = t: the phases merged in a fixed order (phase 0 always holds
-  // split 0, so M is finite)
+  // partial 0, so M is finite)
   const int c = t;
   float M = -INFINITY;
 #pragma unroll
@@ -847,12 +896,6 @@ hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* ac
   return hipSuccess;
 }
 
-hipError_t launch_gsum(const uint16_t* act, int B, int K, int G, float2* gsum, hipStream_t st) {
-  gsum_kernel<<<dim3(K / G, B), 64, 0, st>>>(act, K, G, gsum);
-  FUTX_LAUNCH_CHECK();
-  return hipSuccess;
-}
-
 hipError_t launch_reduce(const float* part, int S, int B, int N, const float* rowscale,
                          const float* resid, float* out, int gateup_inter, hipStream_t st) {
   const int total = B * N;
@@ -861,9 +904,9 @@ hipError_t launch_reduce(const float* part, int S, int B, int N, const float* ro
   return hipSuccess;
 }
 
-hipError_t launch_swiglu(const float* part, int S, int B, int I, int G, const float* invr,
-                         uint16_t* act, float2* gsum, hipStream_t st) {
-  swiglu_kernel<<<dim3(I / G, B), G, 0, st>>>(part, S, B, I, G, invr, act, gsum);
+hipError_t launch_swiglu(const float* part, int S, int B, int I, const float* invr, uint16_t* act,
+                         hipStream_t st) {
+  swiglu_kernel<<<dim3((I + 255) / 256, B), 256, 0, st>>>(part, S, B, I, invr, act);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -880,19 +923,26 @@ hipError_t launch_kv_append(const float* k, const float* v, const int32_t* posit
   return hipSuccess;
 }
 
-hipError_t launch_attn_decode(const float* qkv, const int32_t* cached_lens, const int32_t* block_table,
-                              int mpps, int B, int nq, int D, const AttnPlan& plan, int hb, float theta,
-                              const KVPtrs& kv, float* wpart, hipStream_t st) {
-  if (nq % kv.nkv != 0 || nq / kv.nkv > 16) return hipErrorInvalidValue;
-  const int nwg = (plan.nsplit + 3) / 4;
-  const dim3 grid(nwg, kv.nkv, B);
-  const float scale = 1.0f / sqrtf((float)D);
+hipError_t launch_attn_decode(AttnArgs a, int B, int D, const AttnPlan& plan, hipStream_t st) {
+  if (a.nq % a.kv.nkv != 0 || a.nq / a.kv.nkv > 16) return hipErrorInvalidValue;
+  a.chunk = plan.chunk;
+  a.nwg = (plan.nsplit + 3) / 4;
+  a.scale = 1.0f / sqrtf((float)D);
+  const dim3 grid(a.nwg, a.kv.nkv, B);
   if (D == 128)
-    attn_decode_kernel<128><<<grid, 256, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, plan.chunk, nwg, hb,
-                                                   theta, scale, kv, wpart);
+    attn_decode_kernel<128><<<grid, 256, 0, st>>>(a);
   else
-    attn_decode_kernel<64><<<grid, 256, 0, st>>>(qkv, nq, cached_lens, block_table, mpps, plan.chunk, nwg, hb,
-                                                  theta, scale, kv, wpart);
+    attn_decode_kernel<64><<<grid, 256, 0, st>>>(a);
+  FUTX_LAUNCH_CHECK();
+  if (a.nwg == 1) return hipSuccess;  // finished in the attention kernel
+  // the workgroup partials: 4 * chunk tokens each
+  const dim3 mgrid(a.nq, B);
+  if (D == 128)
+    attn_merge_kernel<128><<<mgrid, 256, 0, st>>>(a.wpart, a.cached_lens, a.nq, 4 * a.chunk, a.nwg, a.hb,
+                                                   a.tmax, a.out_f32, a.out_bf16, a.term_stride);
+  else
+    attn_merge_kernel<64><<<mgrid, 256, 0, st>>>(a.wpart, a.cached_lens, a.nq, 4 * a.chunk, a.nwg, a.hb, a.tmax,
+                                                  a.out_f32, a.out_bf16, a.term_stride);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }
@@ -914,35 +964,16 @@ AttnPlan attn_plan(int B, int nkv, int max_context) {
   return p;
 }
 
-hipError_t launch_attention(const void* q, bool q_f32, const int32_t* lens, int len_add,
-                            const int32_t* block_table, int mpps, int B, int nq, int D,
-                            const AttnPlan& plan, const KVPtrsConst& kv, float* apart,
-                            hipStream_t st) {
-  const dim3 grid(plan.nsplit, kv.nkv, B);
-  const float scale = 1.0f / sqrtf((float)D);
-#define FUTX_ATTN(DD, QF)                                                                          \
-  attn_split_kernel<DD, QF><<<grid, 64, 0, st>>>(q, lens, len_add, block_table, mpps, nq, plan.chunk, \
-                                                 plan.nsplit, scale, kv, apart)
-  if (D == 128) {
-    if (q_f32) FUTX_ATTN(128, true); else FUTX_ATTN(128, false);
-  } else {
-    if (q_f32) FUTX_ATTN(64, true); else FUTX_ATTN(64, false);
-  }
-#undef FUTX_ATTN
-  FUTX_LAUNCH_CHECK();
-  return hipSuccess;
-}
-
-hipError_t launch_attn_merge(const float* apart, const int32_t* lens, int len_add, int B, int nq,
-                             int D, const AttnPlan& plan, int hb, float* out_f32,
-                             uint16_t* out_bf16, size_t term_stride, hipStream_t st) {
-  const dim3 grid(nq, B);
-  if (D == 128)
-    attn_merge_kernel<128><<<grid, 256, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride);
-  else
-    attn_merge_kernel<64><<<grid, 256, 0, st>>>(apart, lens, len_add, nq, plan.chunk, plan.nsplit, hb, out_f32, out_bf16, term_stride);
-  FUTX_LAUNCH_CHECK();
-  return hipSuccess;
+// attn_plan(B, nkv, c).nsplit <= this bound for every c <= max_context: with
+// one page per split nsplit = pages <= FUTX_ATTN_SPLITS / (B nkv); with more,
+// pages / chunk pages <= FUTX_ATTN_SPLITS / (B nkv).  The bound does not
+// decrease with the context, so a workspace sized with it fits every shorter
+// context too.
+int attn_nsplit_bound(int B, int nkv, int max_context) {
+  const long pages = (max_context + kPageSize - 1) / kPageSize;
+  const long cap = (FUTX_ATTN_SPLITS + (long)B * nkv - 1) / ((long)B * nkv);
+  const long n = pages < cap ? pages : cap;
+  return n < 1 ? 1 : (int)n;
 }
 
 }  // namespace futx

@@ -30,9 +30,8 @@ FUTX_PROJ_QKV, FUTX_PROJ_O, FUTX_PROJ_GATEUP, FUTX_PROJ_DOWN = 0, 1, 2, 3
 PROJ_BY_NAME = {"qkv": 0, "o": 1, "gateup": 2, "down": 3}
 
 # stages of futx_decode_block (futx_decode_block_stage)
-(FUTX_STAGE_QKV, FUTX_STAGE_ROTATE_APPEND, FUTX_STAGE_ATTENTION, FUTX_STAGE_MERGE, FUTX_STAGE_O, FUTX_STAGE_GATEUP,
- FUTX_STAGE_DOWN) = range(7)
-FUTX_STAGE_COUNT = 7
+(FUTX_STAGE_QKV, FUTX_STAGE_ATTENTION, FUTX_STAGE_O, FUTX_STAGE_GATEUP, FUTX_STAGE_DOWN) = range(5)
+FUTX_STAGE_COUNT = 5
 
 FUTX_KV_ROPE = 1
 FUTX_KV_HADAMARD = 2
@@ -262,10 +261,10 @@ def futx_int4_linear(dims, proj, qweight, batch, act, out, workspace, workspace_
                                                      int(workspace_bytes), _stream(stream)))
 
 
-def futx_decode_attention(dims, batch, q_rot, lens, block_table, max_pages_per_seq, max_context, cache, out,
+def futx_decode_attention(dims, batch, qkv, cached_lens, block_table, max_pages_per_seq, max_context, cache, out,
                           workspace, workspace_bytes, stream=None):
     _check("futx_decode_attention", _lib.futx_decode_attention(ctypes.byref(make_dims(dims)), int(batch),
-                                                               _ptr(q_rot), _ptr(lens), _ptr(block_table),
+                                                               _ptr(qkv), _ptr(cached_lens), _ptr(block_table),
                                                                int(max_pages_per_seq), int(max_context),
                                                                ctypes.byref(cache), _ptr(out), _ptr(workspace),
                                                                int(workspace_bytes), _stream(stream)))

@@ -93,14 +93,54 @@ def flip_tolerant(got_q, got_s, x64, tag, max_frac=1e-4, max_per_row=None):
     return st
 
 
+class DecodedCache:
+    """A host copy of a device KV cache decoded once (tests/layouts.py):
+    codes K, V [page][nkv][64][d] and scales KS, VS [page][nkv][64]."""
+
+    def __init__(self, cache_host, dims, num_pages):
+        from . import layouts
+
+        kc, vc, ks, vs = cache_host
+        self.K, self.KS, self.V, self.VS = layouts.decode_cache(kc, vc, ks, vs, num_pages, dims.n_kv_heads,
+                                                                dims.head_dim)
+
+    def tokens(self, slots):
+        p, o = np.asarray(slots) // 64, np.asarray(slots) % 64
+        return self.K[p, :, o], self.KS[p, :, o], self.V[p, :, o], self.VS[p, :, o]
+
+
 def cache_tokens(cache_host, dims, num_pages, slots):
     """Codes and scales of the given cache slots: K [n][nkv][d], KS [n][nkv], V, VS."""
-    from . import layouts
+    dec = cache_host if isinstance(cache_host, DecodedCache) else DecodedCache(cache_host, dims, num_pages)
+    return dec.tokens(slots)
 
-    kc, vc, ks, vs = cache_host
-    K, KS, V, VS = layouts.decode_cache(kc, vc, ks, vs, num_pages, dims.n_kv_heads, dims.head_dim)
-    p, o = np.asarray(slots) // 64, np.asarray(slots) % 64
-    return K[p, :, o], KS[p, :, o], V[p, :, o], VS[p, :, o]
+
+def oracle_history(decoded, dims, layout, b, k, v, cap, stats):
+    """The oracle's cache of sequence b with len(k) history tokens at
+    positions 0.. (pre-RoPE fp32 k, v [L][nkv][d]) and room for `cap` tokens.
+    The oracle rotates them in fp64 (RoPE, block Hadamard) and quantizes them
+    by its fp32 recipe; where the device, which rotated them in fp32, stored a
+    code or scale on the other side of a rounding boundary (flip_tolerant: at
+    most one code per token and head, within CODE_WINDOW of a midpoint), the
+    oracle continues with the device's choice, as it does for the new token.
+    decoded: the device cache (DecodedCache), or None for the oracle's own
+    codes throughout."""
+    L = len(k)
+    c = oracle.LogicalKVCache.empty(cap, dims.n_kv_heads, dims.head_dim)
+    if L == 0:
+        return c
+    pos = np.arange(L)
+    if decoded is None:
+        oracle.history_fill(c, k, v, pos, dims)
+        return c
+    k_rot, v_rot = oracle.rotate_kv(np.asarray(k, np.float64), np.asarray(v, np.float64), pos[:, None], dims)
+    slots = layout.block_table[b, pos // layout.page_size].astype(np.int64) * layout.page_size + pos % layout.page_size
+    K, KS, V, VS = decoded.tokens(slots)
+    stats.add(flip_tolerant(K, KS, k_rot, ("history key", b), max_per_row=1))
+    stats.add(flip_tolerant(V, VS, v_rot, ("history value", b), max_per_row=1))
+    c.k_codes[:L], c.k_scales[:L] = K, KS
+    c.v_codes[:L], c.v_scales[:L] = V, VS
+    return c
 
 
 def block_tolerance(ref):
@@ -153,7 +193,7 @@ class BlockCase:
         at most one flipped code per (token, KV head) row)."""
         d = self.dims
         slots = np.array([self.layout.slot(b, int(L)) for b, L in enumerate(self.lens)], np.int32)
-        K, KS, V, VS = cache_tokens(self.gpu_cache, d, self.layout.num_pages, slots)
+        K, KS, V, VS = self.gpu_decoded.tokens(slots)
         self.kv_flips = FlipStats()
 
         def hook(b, kc, ks, vc, vs, k_rot, v_rot):
@@ -165,23 +205,26 @@ class BlockCase:
         return hook
 
     def run_oracle(self, gpu_codes=True):
-        """The oracle block; with gpu_codes (after run_gpu), the new token's
-        boundary-case codes follow the GPU's choice (gpu_kv_hook)."""
+        """The oracle block; with gpu_codes (after run_gpu), boundary-case
+        codes of the history (oracle_history) and of the new token
+        (gpu_kv_hook) follow the GPU's choice."""
         d = self.dims
         t0 = time.time()
         qw = oracle.quantize_block_weights(self.w, d)
+        host = getattr(self, "gpu_cache", None) if gpu_codes else None
+        self.gpu_decoded = DecodedCache(host, d, self.layout.num_pages) if host is not None else None
+        self.hist_flips = FlipStats()
         caches = []
         for b, (k, v) in enumerate(self.hist):
-            L = int(self.lens[b])
-            c = oracle.LogicalKVCache.empty(L + 1, d.n_kv_heads, d.head_dim)
-            if L:
-                oracle.history_fill(c, k, v, np.arange(L), d)
-            caches.append(c)
+            caches.append(oracle_history(self.gpu_decoded, d, self.layout, b, k, v, int(self.lens[b]) + 1,
+                                         self.hist_flips))
+            if b % 8 == 7:
+                say("oracle history", b + 1, "of", len(self.hist), "sequences")
         diag = {}
-        hook = self.gpu_kv_hook() if gpu_codes and getattr(self, "gpu_cache", None) is not None else None
+        hook = self.gpu_kv_hook() if host is not None else None
         y = oracle.decode_block(self.x, qw, caches, self.lens, d, diag=diag, kv_hook=hook)
         if hook is not None:
-            say("new-token boundary decisions taken from the GPU:", self.kv_flips)
+            say("boundary decisions taken from the GPU: history", self.hist_flips, "; new token", self.kv_flips)
         self.oracle_caches, self.diag = caches, diag
         say("oracle done in %.1fs" % (time.time() - t0))
         return y

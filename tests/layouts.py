@@ -18,12 +18,12 @@ import numpy as np
 
 def _nibbles(words):
     """uint32 [...] -> codes int8 [..., 8] in element order e = 0..7."""
-    w = np.asarray(words, np.uint64)
-    out = np.empty(words.shape + (8,), np.int8)
+    w = np.asarray(words, np.uint32)
+    out = np.empty(w.shape + (8,), np.int8)
     for e in range(8):
         r = 4 * (e // 2) + 16 * (e % 2)
-        rot = ((w >> np.uint64(r)) | (w << np.uint64(32 - r))) & np.uint64(0xFFFFFFFF) if r else w
-        out[..., e] = ((rot >> np.uint64(3)) & np.uint64(15)).astype(np.int16) - 8
+        rot = (w >> np.uint32(r)) | (w << np.uint32(32 - r)) if r else w
+        out[..., e] = ((rot >> np.uint32(3)) & np.uint32(15)).astype(np.int8) - 8
     return out
 
 
@@ -88,11 +88,20 @@ def decode_v_page(vbytes, d):
 
 
 def decode_cache(k_codes, v_codes, k_scales, v_scales, num_pages, nkv, d):
-    """Whole cache -> (k codes [pages][nkv][64][d], k scales fp16 [pages][nkv][64], v codes, v scales)."""
-    kc = np.asarray(k_codes, np.uint8).reshape(num_pages, nkv, 64 * d // 2)
-    vc = np.asarray(v_codes, np.uint8).reshape(num_pages, nkv, 64 * d // 2)
-    K = np.stack([np.stack([decode_k_page(kc[p, h], d) for h in range(nkv)]) for p in range(num_pages)])
-    V = np.stack([np.stack([decode_v_page(vc[p, h], d) for h in range(nkv)]) for p in range(num_pages)])
-    ks = np.asarray(k_scales).view(np.float16).reshape(num_pages, nkv, 64)
-    vs = np.asarray(v_scales).view(np.float16).reshape(num_pages, nkv, 64)
+    """Whole cache -> (k codes [pages][nkv][64][d], k scales fp16 [pages][nkv][64], v codes, v scales).
+
+    The same index maps as decode_k_page / decode_v_page, over all pages and
+    heads at once: key token tt*16 + i, channel 32 s + 8 g + e; value token
+    tb*32 + 16 h + 4 g + e4 (element e = 4 h + e4), channel cg*64 + 16 c4 + i."""
+    P = num_pages
+    kb = np.asarray(k_codes, np.uint8).reshape(P, nkv, 4, 4, 16, d // 32, 4)  # tt g i s byte
+    kw = kb.copy().view(np.uint32)[..., 0]
+    K = _nibbles(kw)  # P h tt g i s e
+    K = K.transpose(0, 1, 2, 4, 5, 3, 6).reshape(P, nkv, 64, d)  # P h tt i s g e
+    vb = np.asarray(v_codes, np.uint8).reshape(P, nkv, 2, d // 64, 4, 16, 4, 4)  # tb cg g i c4 byte
+    vw = vb.copy().view(np.uint32)[..., 0]
+    V = _nibbles(vw).reshape(P, nkv, 2, d // 64, 4, 16, 4, 2, 4)  # P h tb cg g i c4 hh e4
+    V = V.transpose(0, 1, 2, 7, 4, 8, 3, 6, 5).reshape(P, nkv, 64, d)  # P h tb hh g e4 cg c4 i
+    ks = np.asarray(k_scales).view(np.float16).reshape(P, nkv, 64)
+    vs = np.asarray(v_scales).view(np.float16).reshape(P, nkv, 64)
     return K, ks, V, vs
