@@ -197,6 +197,15 @@ def _full_step(DB, batch, sample, tables):
     np.testing.assert_array_equal(xs[0], np.asarray(emb, np.float32)[toks])
     ratios = []
     x_chain = xs[0][sample].astype(np.float64)
+    # the oracle's own sensitivity to differences of the size an
+    # implementation makes: a second oracle chain that receives, after each
+    # layer, seeded Gaussian noise with the RMS of the GPU's deviation from
+    # the oracle on that layer's input (a one-ulp change of the input alone
+    # stays at 2e-6 through all 32 layers; the GPU's per-layer deviations,
+    # within tolerance, are fp32-versus-fp64 decisions at the bf16 rounding
+    # points and are far larger than an ulp)
+    noise = np.random.default_rng(77)
+    x_pert = xs[0][sample].astype(np.float64)
     hist_flips = FlipStats()
     for li in range(wl.n_layers):
         # the layer's history as the device wrote it, boundary cases checked
@@ -205,42 +214,54 @@ def _full_step(DB, batch, sample, tables):
               for b in sample]
         del dec
         ref = oracle.decode_block(xs[li][sample], qws[li], oc, lens[sample], d)
-        # the chained block rewrites slot L of the same caches with its own token
+        # the chained blocks rewrite slot L of the same caches with their own tokens
         x_chain = oracle.decode_block(x_chain.astype(np.float32), qws[li], oc, lens[sample], d)
+        x_pert = oracle.decode_block(x_pert.astype(np.float32), qws[li], oc, lens[sample], d)
         qws[li].drop_dense()
-        err = float(np.max(np.abs(xs[li + 1][sample] - ref)))
+        dev = xs[li + 1][sample] - ref
+        x_pert = x_pert + noise.normal(0.0, float(np.sqrt(np.mean(dev * dev))), x_pert.shape)
+        err = float(np.max(np.abs(dev)))
         tol = block_tolerance(ref)
         ratios.append(err / tol)
-        say("layer %d block err %.3g tol %.3g; chained drift %.3g" % (
-            li, err, tol, float(np.max(np.abs(xs[li + 1][sample] - x_chain)))))
+        say("layer %d block err %.3g tol %.3g; chained drift: gpu vs oracle %.3g, oracle vs noisy oracle %.3g" % (
+            li, err, tol, float(np.max(np.abs(xs[li + 1][sample] - x_chain))), float(np.max(np.abs(x_pert - x_chain)))))
         assert err <= tol, (li, err, tol)
     say("worst layer err / tol %.3f; history boundary decisions taken from the GPU: %s" % (max(ratios), hist_flips))
     del caches
     ref, ref_top1 = oracle_head(xs[-1][sample], folded, d.rms_eps)
     chain_logits, chain_top1 = oracle_head(x_chain, folded, d.rms_eps)
-    return g_logits[sample], g_top1[sample], ref, ref_top1, chain_logits, chain_top1
+    pert_logits, pert_top1 = oracle_head(x_pert, folded, d.rms_eps)
+    self_drift = np.max(np.abs(pert_logits - chain_logits), axis=1)
+    say("oracle chain vs noisy oracle chain: logits drift", np.round(self_drift, 4).tolist(), "top-1",
+        chain_top1.tolist(), "vs", pert_top1.tolist())
+    return g_logits[sample], g_top1[sample], ref, ref_top1, chain_logits, chain_top1, self_drift
 
 
-def check_chained_top1(got_logits, got_top1, chain_logits, chain_top1, what):
-    """The GPU's chained step against the oracle's chained step: the top-1
-    tokens agree, or the oracle's logits of the two tokens lie within the
-    logits tolerance of each other.  The chained logits themselves differ by
-    the drift of two chains that take different boundary decisions (measured,
-    not bounded: see the teacher-forcing note above)."""
+def check_chained_top1(got_logits, got_top1, chain_logits, chain_top1, self_drift, what):
+    """The GPU's chained step against the oracle's chained step.  Over 32
+    layers two correct chains that take different boundary decisions (bf16
+    operands, INT4 cache codes) drift apart; the drift of the oracle chain
+    against itself with per-layer noise of the GPU's measured per-layer
+    deviation (self_drift, per row) measures how far the chained logits are
+    determined at that level.  Rule: the top-1 tokens agree, or the oracle
+    chain's logits of the two tokens lie within the one-step logits
+    tolerance plus twice that drift of each other."""
     tol = block_tolerance(chain_logits)
-    say(what, "chained logits drift %.3g (tolerance of one step %.3g)" % (
+    say(what, "chained logits drift gpu vs oracle %.3g (one-step tolerance %.3g)" % (
         float(np.max(np.abs(got_logits - chain_logits))), tol))
     for b in range(chain_logits.shape[0]):
         gap = chain_logits[b, chain_top1[b]] - chain_logits[b, got_top1[b]]
-        say(what, "row", b, "top-1 gpu", int(got_top1[b]), "oracle chain", int(chain_top1[b]), "oracle gap %.3g" % gap)
-        assert got_top1[b] == chain_top1[b] or gap <= tol, (what, b, gap, tol)
+        lim = tol + 2.0 * float(self_drift[b])
+        say(what, "row", b, "top-1 gpu", int(got_top1[b]), "oracle chain", int(chain_top1[b]),
+            "oracle gap %.3g, limit %.3g (oracle self-drift %.3g)" % (gap, lim, float(self_drift[b])))
+        assert got_top1[b] == chain_top1[b] or gap <= lim, (what, b, gap, lim)
 
 
 @pytest.mark.slow
 def test_full_step_8b_batch1(F, DB, tables):
-    g, gt, r, rt, cl, ct = _full_step(DB, 1, [0], tables)
+    g, gt, r, rt, cl, ct, sd = _full_step(DB, 1, [0], tables)
     check_logits(g, gt, r, rt, "8B step b1 L8192 (LM head on the step's final state)")
-    check_chained_top1(g, gt, cl, ct, "8B step b1 L8192 (chained)")
+    check_chained_top1(g, gt, cl, ct, sd, "8B step b1 L8192 (chained)")
 
 
 @pytest.mark.slow
@@ -248,6 +269,6 @@ def test_full_step_8b_batch16_sampled(F, DB, tables):
     # one row of each batch position class b % 4 (the matrix-core row of a
     # sequence is 4 (b % 4) + b / 4)
     rows = [0, 5, 10, 15]
-    g, gt, r, rt, cl, ct = _full_step(DB, 16, rows, tables)
+    g, gt, r, rt, cl, ct, sd = _full_step(DB, 16, rows, tables)
     check_logits(g, gt, r, rt, "8B step b16 L8192 rows %s" % rows)
-    check_chained_top1(g, gt, cl, ct, "8B step b16 L8192 rows %s (chained)" % rows)
+    check_chained_top1(g, gt, cl, ct, sd, "8B step b16 L8192 rows %s (chained)" % rows)
