@@ -226,6 +226,21 @@ futx_status futx_decode_block(const futx_dims* dims, const futx_block_weights* w
                               const futx_kv_cache* cache, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* futx_decode_block without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels, launch order
+ * and results as futx_decode_block, with the workspace taken from a static
+ * device buffer of 72 MiB that the library holds on each GPU it runs on
+ * until the process ends (enough for the 70B shape at batch 32).  It calls
+ * no allocating routine.  FUTX_E_WORKSPACE if batch and max_context need
+ * more scratch than that (use futx_decode_block).  Every call on a GPU
+ * shares that GPU's buffer: calls that overlap on one GPU (several streams
+ * or threads) race; calls on one stream run in order. */
+futx_status futx_decode_block_noalloc(const futx_dims* dims, const futx_block_weights* w, int32_t batch,
+                                      float* x, const int32_t* cached_lens, const int32_t* block_table,
+                                      int32_t max_pages_per_seq, int32_t max_context,
+                                      const futx_kv_cache* cache, void* stream);
+
 /* Stages of futx_decode_block, in launch order (one kernel each; the
  * attention stage adds a merge kernel when the plan splits a sequence over
  * more than one workgroup). */

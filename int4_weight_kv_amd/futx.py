@@ -96,6 +96,8 @@ _SIGS = {
     "futx_decode_workspace_size": (_I32, [_D, _I32, _I32, _SZ]),
     "futx_decode_block": (_I32, [_D, ctypes.POINTER(futx_block_weights), _I32, _P, _P, _P, _I32, _I32,
                                  ctypes.POINTER(futx_kv_cache), _P, ctypes.c_size_t, _P]),
+    "futx_decode_block_noalloc": (_I32, [_D, ctypes.POINTER(futx_block_weights), _I32, _P, _P, _P, _I32, _I32,
+                                         ctypes.POINTER(futx_kv_cache), _P]),
     "futx_decode_block_stage": (_I32, [_D, ctypes.POINTER(futx_block_weights), _I32, _P, _P, _P, _I32, _I32,
                                        ctypes.POINTER(futx_kv_cache), _P, ctypes.c_size_t, _I32, _P]),
     "futx_int4_linear": (_I32, [_D, _I32, ctypes.POINTER(futx_qweight), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -243,6 +245,14 @@ def futx_decode_block(dims, weights, batch, x, cached_lens, block_table, max_pag
                                                        int(max_pages_per_seq), int(max_context),
                                                        ctypes.byref(cache), _ptr(workspace), int(workspace_bytes),
                                                        _stream(stream)))
+
+
+def futx_decode_block_noalloc(dims, weights, batch, x, cached_lens, block_table, max_pages_per_seq, max_context,
+                              cache, stream=None):
+    _check("futx_decode_block_noalloc",
+           _lib.futx_decode_block_noalloc(ctypes.byref(make_dims(dims)), ctypes.byref(weights), int(batch), _ptr(x),
+                                          _ptr(cached_lens), _ptr(block_table), int(max_pages_per_seq),
+                                          int(max_context), ctypes.byref(cache), _stream(stream)))
 
 
 def futx_decode_block_stage(dims, weights, batch, x, cached_lens, block_table, max_pages_per_seq, max_context,

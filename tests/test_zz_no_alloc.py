@@ -1,0 +1,84 @@
+"""futx_decode_block_noalloc (the decode block on the library's static
+scratch, for callers that cannot allocate) against futx_decode_block with a
+caller workspace: bit-identical block outputs on two calls in a row, the
+second with a smaller batch and shorter contexts, both through the C ABI."""
+
+import numpy as np
+import pytest
+
+from int4_weight_kv_amd import workload as W
+from tests.gpu_common import say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from int4_weight_kv_amd import futx
+
+    return futx
+
+
+def _case(F, DB, wl, lens, layer):
+    d = wl.dims
+    layout = W.page_layout(wl, lens, extra_tokens=1, seed=3, spare_pages=2)
+    layer_dev = DB.DeviceLayer(d, W.block_weights(wl, 0))
+    cache = DB.DeviceKVCache(d, layout.num_pages)
+    for b, L in enumerate(lens):
+        k, v = W.history(wl, 0, b, int(L))
+        DB.fill_history(cache, k, v, layout, b)
+    return d, layout, layer_dev, cache
+
+
+@pytest.mark.parametrize("shape", ["tiny", "8b"])
+def test_noalloc_matches_workspace_entry(F, shape):
+    from int4_weight_kv_amd import block as DB
+
+    dims = W.TINY if shape == "tiny" else W.LLAMA8B
+    calls = [(8, "uniform:300:2100"), (3, "uniform:1:700")]  # the second call is smaller
+    for i, (batch, lengths) in enumerate(calls):
+        wl = W.Workload(f"noalloc-{shape}-{i}", dims, batch, lengths)
+        lens = wl.cached_lengths(0)
+        d, layout, layer, cache = _case(F, DB, wl, lens, i)
+        mc = int(lens.max()) + 1
+        lens_d = torch.from_numpy(lens).cuda()
+        table = torch.from_numpy(layout.block_table).cuda()
+        x0 = torch.from_numpy(W.hidden_state(wl)).cuda()
+        # the existing entry point, with its own workspace
+        ws_bytes = F.futx_decode_workspace_size(d, batch, mc)
+        ws = DB.device_buffer(ws_bytes)
+        x_ref = x0.clone()
+        say("noalloc", shape, "call", i, "batch", batch, "lens", lens.tolist(), "max_context", mc)
+        F.futx_decode_block(d, layer.c_weights, batch, x_ref, lens_d, table, layout.block_table.shape[1], mc,
+                            cache.c_cache, ws, ws_bytes)
+        torch.cuda.synchronize()
+        # the no-allocation entry point on the same cache (it rewrites the
+        # same new-token slots with the same codes)
+        x_na = x0.clone()
+        F.futx_decode_block_noalloc(d, layer.c_weights, batch, x_na, lens_d, table, layout.block_table.shape[1], mc,
+                                    cache.c_cache)
+        torch.cuda.synchronize()
+        a, b = x_ref.cpu().numpy(), x_na.cpu().numpy()
+        assert np.all(np.isfinite(a))
+        np.testing.assert_array_equal(b, a)
+        say("  bit-identical to futx_decode_block; max|x| %.3g" % float(np.max(np.abs(a))))
+
+
+def test_noalloc_rejects_oversized_request(F):
+    from int4_weight_kv_amd import block as DB
+
+    # 70B shape at batch 32 fits; a workspace need beyond the buffer is refused
+    # before any launch (the dims check runs first, so no device buffers are read)
+    d = W.Dims(8192, 64, 8, 128, 57344, 128, 64)
+    wl = W.Workload("noalloc-big", d, 32, "fixed:8")
+    need = F.futx_decode_workspace_size(d, 32, 9)
+    say("a block needing", need, "bytes of scratch")
+    dummy = DB.device_buffer(256)
+    w = F.make_block_weights(*((dummy, dummy),) * 4)
+    cache = F.make_cache(dummy, dummy, dummy, dummy, 1)
+    with pytest.raises(F.FutxError) as e:
+        F.futx_decode_block_noalloc(d, w, 32, dummy, dummy, dummy, 1, 9, cache)
+    assert e.value.status == F.FUTX_E_WORKSPACE
