@@ -328,6 +328,19 @@ futx_status futx_lm_head_workspace_size(const futx_dims* dims, int32_t vocab, in
 futx_status futx_fold_head(int32_t vocab, int32_t hidden, const uint16_t* w_bf16_host,
                            const float* gain_host, uint16_t* out_bf16_host);
 
+/* ------------------------------------------------------------- measurement */
+
+/* Plain streaming read of `bytes` (a positive multiple of 16) of device
+ * memory at `buf` (16-byte aligned) by `workgroups` workgroups of 256
+ * threads, each reading one contiguous chunk with 128-bit loads: the
+ * achievable HBM read bandwidth that the decode kernels are compared with
+ * (decode is bound by weight and KV-cache reads: kongchang.com/en article,
+ * section "Why do Prefill and Decode need different quantization
+ * strategies?").  sink: uint32 [workgroups] (dev), written only in the rare
+ * case that a workgroup's XOR of its data equals a fixed value (it keeps the
+ * loads from being optimized away). */
+futx_status futx_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

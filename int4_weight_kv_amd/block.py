@@ -121,6 +121,15 @@ class DecodeRunner:
                                   stream)
 
 
+def bf16_bits(values):
+    """bf16 bit patterns of fp32 values, rounded to nearest even (values that
+    are already bf16 keep their bits; NaN stays NaN)."""
+    u = np.ascontiguousarray(values, np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = ((u + (0x7FFF + ((u >> 16) & 1))) >> 16).astype(np.uint16)
+    return np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), r)
+
+
 class DecodeHead:
     """Embedding table and LM head (final norm gain folded in, bf16) on the device."""
 
@@ -128,8 +137,8 @@ class DecodeHead:
         torch = _torch()
         self.dims = dims
         self.vocab, hidden = emb_values.shape
-        emb_bits = (np.ascontiguousarray(emb_values, np.float32).view(np.uint32) >> 16).astype(np.uint16)
-        head_bits = (np.ascontiguousarray(head_values, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        emb_bits = bf16_bits(emb_values)
+        head_bits = bf16_bits(head_values)
         folded = np.empty_like(head_bits)
         F.futx_fold_head(self.vocab, hidden, head_bits, final_gain, folded)
         self.emb = torch.from_numpy(emb_bits.view(np.int16)).to(device)

@@ -107,6 +107,7 @@ _SIGS = {
     "futx_lm_head": (_I32, [_D, _I32, _P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "futx_lm_head_workspace_size": (_I32, [_D, _I32, _I32, _SZ]),
     "futx_fold_head": (_I32, [_I32, _I32, _P, _P, _P]),
+    "futx_stream_read": (_I32, [_P, ctypes.c_size_t, _P, _I32, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -303,3 +304,8 @@ def futx_fold_head(vocab, hidden, w_bf16_host, gain_host, out_bf16_host):
     gain = np.ascontiguousarray(gain_host, np.float32)  # kept alive across the call
     _check("futx_fold_head", _lib.futx_fold_head(int(vocab), int(hidden), _ptr(w_bf16_host), _ptr(gain),
                                                  _ptr(out_bf16_host)))
+
+
+def futx_stream_read(buf, nbytes, sink, workgroups, stream=None):
+    _check("futx_stream_read", _lib.futx_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(workgroups),
+                                                     _stream(stream)))

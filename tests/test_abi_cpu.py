@@ -256,3 +256,17 @@ def test_fold_head_matches_oracle(fx):
     fx.futx_fold_head(vocab, hidden, wbits, gain, out)
     got = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     np.testing.assert_array_equal(got, oracle.fold_head(w, gain))
+
+
+def test_head_tables_round_to_nearest_even():
+    """DecodeHead's fp32 -> bf16 conversion rounds to nearest even (torch's
+    cast), so tables that are not already bf16-valued are not truncated."""
+    torch = pytest.importorskip("torch")
+    from int4_weight_kv_amd.block import bf16_bits
+
+    r = np.random.default_rng(3)
+    ties = ((r.integers(0x3F000000, 0x40800000, 4000, dtype=np.uint32) & 0xFFFF0000) | 0x8000).view(np.float32)
+    x = np.concatenate([r.standard_normal(50000).astype(np.float32), ties,
+                        np.array([np.inf, -np.inf, 0.0, -0.0, 3.0e38, 1e-40], np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bf16_bits(x), want)
