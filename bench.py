@@ -1,7 +1,7 @@
 """Benchmark of the INT4 decode block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b-b1]
-                    [--phase all|block|dominant|copy|stages|read]
+                    [--phase all|block|dominant|copy|stages|read|fp8]
                     [--no-sweep] [--no-cpu-baseline]
 
 Workloads: 8b-b<B>, 8b-ragged-b<B>, 70b-b<B>, tiny-b<B> (one block), and
@@ -36,7 +36,8 @@ The default run (the 8B block at batch 1, 2048 cached tokens) reports:
 
 --phase dominant runs only the gate/up stage (counter collection), --phase
 copy a plain device copy of known size (counter calibration), --phase read
-the streaming read alone, --phase stages every stage of the block alone.
+the streaming read alone, --phase stages every stage of the block alone,
+--phase fp8 the 8B projections as INT4 and as FP8 (e4m3) side by side.
 """
 
 import argparse
@@ -459,6 +460,56 @@ def full_step_sweep(torch, timer, measured, batches=(1, 16)):
 # ------------------------------------------------------------------ phases
 
 
+def fp8_phase(torch, F, timer, batches=(1, 8, 16, 32)):
+    """The four 8B projections as INT4 (futx_int4_linear) and as FP8 e4m3
+    weights and activations (futx_fp8_linear), us per call, each cycling
+    enough weight copies to exceed the Infinity Cache; weights drawn on the
+    device (the timing does not depend on the values)."""
+    from int4_weight_kv_amd import block as DB
+    from int4_weight_kv_amd import workload as W
+
+    d = W.LLAMA8B
+    shapes = {"qkv": (d.n_qkv, d.hidden), "o": (d.hidden, d.n_heads * d.head_dim),
+              "gateup": (2 * d.intermediate, d.hidden), "down": (d.hidden, d.intermediate)}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(500)
+    res = {"phase": "fp8", "shape": "Llama-3.1-8B projections", "unit": "us", "rows": []}
+    for proj, (n, k) in shapes.items():
+        w = (torch.randn((n, k), generator=g, device="cuda") * 0.02).cpu().numpy()
+        copies = max(3, int(np.ceil(800e6 / (n * k))))
+        int4 = [DB.pack_projection(d, proj, w, None) for _ in range(copies)]
+        f8 = []
+        for _ in range(copies):
+            pb, sb = F.futx_fp8_packed_sizes(d, proj)
+            p, s_ = DB.device_buffer(pb), DB.device_buffer(sb)
+            F.futx_pack_fp8_weights(d, proj, w, None, p, s_)
+            f8.append((p, s_))
+        for B in batches:
+            act = torch.randn((B, k), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+            out = torch.empty((B, n), dtype=torch.float32, device="cuda")
+            ws4 = F.futx_decode_workspace_size(d, B, 1)
+            ws8 = F.futx_fp8_linear_workspace_size(d, proj, B)
+            wsb = DB.device_buffer(max(ws4, ws8))
+            st = timer.stream.cuda_stream
+            f4 = lambda i: F.futx_int4_linear(d, proj, (int4[i % copies].packed, int4[i % copies].scales), B, act,
+                                              out, wsb, ws4, st)
+            f8f = lambda i: F.futx_fp8_linear(d, proj, f8[i % copies], B, act, out, wsb, ws8, st)
+            row = {"proj": proj, "batch": B, "N": n, "K": k}
+            for name, fn, nbytes in (("int4", f4, n * k // 2 + n * (k // 128) * 2),
+                                     ("fp8", f8f, n * k + n * (k // 128) * 4)):
+                timer.run(fn, copies)
+                ms, cnt = timer.timed([(timer.capture(fn, 2 * copies), 2 * copies)], 4)
+                us = ms * 1e3 / cnt
+                row[name + "_us"] = round(us, 2)
+                row[name + "_weight_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            row["int4_speedup"] = round(row["fp8_us"] / row["int4_us"], 3)
+            res["rows"].append(row)
+            log("fp8", json.dumps(row))
+        del int4, f8
+        torch.cuda.empty_cache()
+    return res
+
+
 def full_step_phase(args, wl, desc):
     """Times the full decode step of the workload's own seeded inputs (32
     distinct layers: the weights alone, 3.6 GB, exceed the Infinity Cache)
@@ -528,7 +579,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="8b-b1")
     ap.add_argument("--layers", type=int, default=0, help="layer instances cycled (default: enough to exceed MALL)")
-    ap.add_argument("--phase", default="all", choices=["all", "block", "dominant", "copy", "stages", "read"])
+    ap.add_argument("--phase", default="all", choices=["all", "block", "dominant", "copy", "stages", "read", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -552,6 +603,10 @@ def main():
     if args.phase == "read":
         gbps, wgs = measure_read(torch, F, timer)
         print(json.dumps({"phase": "read", "measured_peak_GBps": gbps, "workgroups": wgs, "bytes": READ_BYTES}))
+        return
+
+    if args.phase == "fp8":
+        print(json.dumps(fp8_phase(torch, F, timer)), flush=True)
         return
 
     wl, desc = workload_by_name(args.workload)

@@ -328,6 +328,55 @@ futx_status futx_lm_head_workspace_size(const futx_dims* dims, int32_t vocab, in
 futx_status futx_fold_head(int32_t vocab, int32_t hidden, const uint16_t* w_bf16_host,
                            const float* gain_host, uint16_t* out_bf16_host);
 
+/* ---------------------------------------------------------- FP8 comparison
+ * The pages set the INT4 decode path against the authors' FP8 path (the
+ * INT4 decode block is 31-51% faster [ABS]).  These entries give the same
+ * projection with e4m3 weights and activations on the fp8 matrix cores.
+ * Format (a reading; the pages give none): OCP e4m3 "fn" bytes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; largest finite 448), one fp32
+ * scale per group of 128 inputs for weight rows and for activation rows,
+ * s = fp32(max|x| / 448), codes e4m3(fp32(x / s)) rounded to nearest even,
+ * saturated at 448.  Rows stay in logical order (gate then up for GATEUP);
+ * the weight bytes are in the fp8 matrix-core operand order (opaque). */
+
+/* Device bytes of an FP8-packed projection: packed = N K, scales = 4 N K / 128. */
+futx_status futx_fp8_packed_sizes(const futx_dims* dims, futx_proj proj, size_t* packed_bytes,
+                                  size_t* scale_bytes);
+
+/* Offline FP8 packing: folds `gain_host` (or NULL) into the columns like
+ * futx_pack_weights, quantizes by the recipe above and writes the device
+ * order.  w_host fp32 [N][K] (host).  Returns after the copies completed. */
+futx_status futx_pack_fp8_weights(const futx_dims* dims, futx_proj proj, const float* w_host,
+                                  const float* gain_host, void* packed_dev, void* scales_dev, void* stream);
+
+/* Same, writing host buffers (no HIP call). */
+futx_status futx_pack_fp8_weights_host(const futx_dims* dims, futx_proj proj, const float* w_host,
+                                       const float* gain_host, void* packed_host, void* scales_host);
+
+/* Workspace bytes of futx_fp8_linear for up to `max_batch` rows (1..32). */
+futx_status futx_fp8_linear_workspace_size(const futx_dims* dims, futx_proj proj, int32_t max_batch,
+                                           size_t* bytes);
+
+/* Activation quantization by the recipe above: act bf16 [rows][k] (dev) ->
+ * codes e4m3 bytes [rows][k] and scales fp32 [rows][k / 128] (dev, caller
+ * owned).  k a positive multiple of 128, rows 1..65535; asynchronous on
+ * `stream`.  The division x / s is IEEE fp32, so the codes equal a host
+ * computation of the same recipe bit for bit. */
+futx_status futx_fp8_quantize_act(int32_t k, int32_t rows, const uint16_t* act, uint8_t* codes, float* scales,
+                                  void* stream);
+
+/* out[b][n] = sum_g s_w[n][g] s_a[b][g] sum_{k in g} w[n][k] a[b][k]: the
+ * activation rows act (bf16 [batch][K], dev) are quantized on the device by
+ * futx_fp8_quantize_act into the workspace, then multiplied on the fp8 matrix
+ * cores; out fp32 [batch][N] (dev).  w: an FP8-packed projection.
+ * Accuracy: the gfx950 fp8 matrix instruction sums each run of 8 products
+ * after truncating them toward zero to 13 bits below the run's largest
+ * operand exponent sum, so the group sums are not exact products summed in
+ * fp32 (the per-output bound is stated with the GPU parity test). */
+futx_status futx_fp8_linear(const futx_dims* dims, futx_proj proj, const futx_qweight* w, int32_t batch,
+                            const uint16_t* act, float* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* ------------------------------------------------------------- measurement */
 
 /* Plain streaming read of `bytes` (a positive multiple of 16) of device

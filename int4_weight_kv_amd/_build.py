@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfutx.so")
 
-HIP_SOURCES = ["kernels.hip", "gemm.hip", "head.hip", "abi.hip", "noalloc.hip", "measure.hip"]
+HIP_SOURCES = ["kernels.hip", "gemm.hip", "head.hip", "abi.hip", "noalloc.hip", "measure.hip", "fp8.hip"]
 CPP_SOURCES = ["pack.cpp"]
 ARCH = "gfx950"
 

@@ -108,6 +108,12 @@ _SIGS = {
     "futx_lm_head_workspace_size": (_I32, [_D, _I32, _I32, _SZ]),
     "futx_fold_head": (_I32, [_I32, _I32, _P, _P, _P]),
     "futx_stream_read": (_I32, [_P, ctypes.c_size_t, _P, _I32, _P]),
+    "futx_fp8_packed_sizes": (_I32, [_D, _I32, _SZ, _SZ]),
+    "futx_pack_fp8_weights": (_I32, [_D, _I32, _P, _P, _P, _P, _P]),
+    "futx_pack_fp8_weights_host": (_I32, [_D, _I32, _P, _P, _P, _P]),
+    "futx_fp8_linear_workspace_size": (_I32, [_D, _I32, _I32, _SZ]),
+    "futx_fp8_quantize_act": (_I32, [_I32, _I32, _P, _P, _P, _P]),
+    "futx_fp8_linear": (_I32, [_D, _I32, ctypes.POINTER(futx_qweight), _I32, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -309,3 +315,46 @@ def futx_fold_head(vocab, hidden, w_bf16_host, gain_host, out_bf16_host):
 def futx_stream_read(buf, nbytes, sink, workgroups, stream=None):
     _check("futx_stream_read", _lib.futx_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(workgroups),
                                                      _stream(stream)))
+
+
+def futx_fp8_packed_sizes(dims, proj):
+    pb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("futx_fp8_packed_sizes", _lib.futx_fp8_packed_sizes(ctypes.byref(make_dims(dims)), _proj(proj),
+                                                               ctypes.byref(pb), ctypes.byref(sb)))
+    return pb.value, sb.value
+
+
+def futx_pack_fp8_weights(dims, proj, w_host, gain_host, packed_dev, scales_dev, stream=None):
+    w_host = np.ascontiguousarray(w_host, dtype=np.float32)
+    g = None if gain_host is None else np.ascontiguousarray(gain_host, dtype=np.float32)
+    _check("futx_pack_fp8_weights", _lib.futx_pack_fp8_weights(ctypes.byref(make_dims(dims)), _proj(proj),
+                                                               _ptr(w_host), _ptr(g), _ptr(packed_dev),
+                                                               _ptr(scales_dev), _stream(stream)))
+
+
+def futx_pack_fp8_weights_host(dims, proj, w_host, gain_host, packed_host, scales_host):
+    w_host = np.ascontiguousarray(w_host, dtype=np.float32)
+    g = None if gain_host is None else np.ascontiguousarray(gain_host, dtype=np.float32)
+    _check("futx_pack_fp8_weights_host", _lib.futx_pack_fp8_weights_host(ctypes.byref(make_dims(dims)), _proj(proj),
+                                                                         _ptr(w_host), _ptr(g), _ptr(packed_host),
+                                                                         _ptr(scales_host)))
+
+
+def futx_fp8_linear_workspace_size(dims, proj, max_batch):
+    b = ctypes.c_size_t()
+    _check("futx_fp8_linear_workspace_size",
+           _lib.futx_fp8_linear_workspace_size(ctypes.byref(make_dims(dims)), _proj(proj), int(max_batch),
+                                               ctypes.byref(b)))
+    return b.value
+
+
+def futx_fp8_quantize_act(k, rows, act, codes, scales, stream=None):
+    _check("futx_fp8_quantize_act", _lib.futx_fp8_quantize_act(int(k), int(rows), _ptr(act), _ptr(codes),
+                                                               _ptr(scales), _stream(stream)))
+
+
+def futx_fp8_linear(dims, proj, qweight, batch, act, out, workspace, workspace_bytes, stream=None):
+    qw = futx_qweight(_ptr(qweight[0]), _ptr(qweight[1])) if isinstance(qweight, tuple) else qweight
+    _check("futx_fp8_linear", _lib.futx_fp8_linear(ctypes.byref(make_dims(dims)), _proj(proj), ctypes.byref(qw),
+                                                   int(batch), _ptr(act), _ptr(out), _ptr(workspace),
+                                                   int(workspace_bytes), _stream(stream)))

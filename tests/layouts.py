@@ -105,3 +105,14 @@ def decode_cache(k_codes, v_codes, k_scales, v_scales, num_pages, nkv, d):
     ks = np.asarray(k_scales).view(np.float16).reshape(P, nkv, 64)
     vs = np.asarray(v_scales).view(np.float16).reshape(P, nkv, 64)
     return K, ks, V, vs
+
+
+def decode_fp8_weights(packed, scales, n, k):
+    """FP8 device order of an [n][k] projection -> (codes uint8 [n][k], fp32
+    scales [n][k // 128]).  Bytes [nt][kb][L][32]: lane L holds row
+    nt*16 + L%16, byte 8 s + e holds input kb*128 + 32 s + 8 (L//16) + e;
+    scales [nt][kb][16]."""
+    b = np.asarray(packed, np.uint8).reshape(n // 16, k // 128, 4, 16, 4, 8)  # nt kb g i s e
+    codes = b.transpose(0, 3, 1, 4, 2, 5).reshape(n, k)  # nt i kb s g e
+    s = np.asarray(scales).view(np.float32).reshape(n // 16, k // 128, 16).transpose(0, 2, 1).reshape(n, k // 128)
+    return codes, s
