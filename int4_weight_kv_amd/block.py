@@ -168,3 +168,118 @@ class DecodeStep:
             if progress is not None:
                 progress(i)
         self.head.lm_head(x, logits, top1, stream)
+
+
+class PagedTable:
+    """Host bookkeeping of a paged KV cache shared by the layers of a model:
+    a free list of physical pages, the block table [batch][max_pages_per_seq]
+    (-1 = no page) and the tokens cached per sequence.  A sequence takes a
+    page from the free list when it first needs a position on it, so prompts
+    of any length sit unpadded and decode steps grow the table one page at a
+    time; release() returns a sequence's pages."""
+
+    def __init__(self, num_pages, batch, max_pages_per_seq, page_size=64, seed=None):
+        order = np.arange(num_pages, dtype=np.int32)
+        if seed is not None:
+            order = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
+        self.free = list(order[::-1])  # taken from the end: the first page taken is order[0]
+        self.page_size = page_size
+        self.table = np.full((batch, max_pages_per_seq), -1, np.int32)
+        self.lens = np.zeros(batch, np.int32)
+        self.dirty = True
+
+    def ensure(self, b, n_tokens):
+        """Pages for positions 0..n_tokens-1 of sequence b."""
+        need = (int(n_tokens) + self.page_size - 1) // self.page_size
+        if need > self.table.shape[1]:
+            raise RuntimeError(f"sequence {b}: {n_tokens} tokens exceed the block table")
+        for j in range(need):
+            if self.table[b, j] < 0:
+                if not self.free:
+                    raise RuntimeError("KV cache out of pages")
+                self.table[b, j] = self.free.pop()
+                self.dirty = True
+
+    def slots(self, b, positions):
+        positions = np.asarray(positions, np.int64)
+        return (self.table[b, positions // self.page_size].astype(np.int64) * self.page_size
+                + positions % self.page_size).astype(np.int32)
+
+    def release(self, b):
+        for j in range(self.table.shape[1]):
+            if self.table[b, j] >= 0:
+                self.free.append(self.table[b, j])
+                self.table[b, j] = -1
+        self.lens[b] = 0
+        self.dirty = True
+
+
+class DecodeSession:
+    """Token-by-token generation for a batch of sequences: unpadded prompts
+    placed in the paged INT4 caches of every layer (futx_kv_append: RoPE,
+    rotation, INT4 at their own positions), then decode steps that take cache
+    pages as sequences cross page boundaries, run the embedding, every block
+    and the LM head through the C ABI, and feed the top-1 token of each
+    sequence back as its next input without leaving the device."""
+
+    def __init__(self, dims, layers, head, batch, num_pages, max_context, page_seed=None, device="cuda"):
+        torch = _torch()
+        self.dims, self.layers, self.head, self.batch = dims, layers, head, int(batch)
+        self.max_context = int(max_context)
+        mpps = (self.max_context + dims.page_size - 1) // dims.page_size
+        self.paged = PagedTable(num_pages, batch, mpps, dims.page_size, page_seed)
+        self.caches = [DeviceKVCache(dims, num_pages, device) for _ in layers]
+        self.table_d = torch.empty((batch, mpps), dtype=torch.int32, device=device)
+        self.lens_d = torch.empty(batch, dtype=torch.int32, device=device)
+        self.ws_bytes = F.futx_decode_workspace_size(dims, batch, self.max_context)
+        self.workspace = device_buffer(self.ws_bytes, device)
+        self.x = torch.empty((batch, dims.hidden), dtype=torch.float32, device=device)
+        self.logits = torch.empty((batch, head.vocab), dtype=torch.float32, device=device)
+        self.top1 = torch.empty(batch, dtype=torch.int32, device=device)
+        self.device = device
+
+    def _sync_metadata(self):
+        torch = _torch()
+        if self.paged.dirty:
+            self.table_d.copy_(torch.from_numpy(self.paged.table))
+            self.paged.dirty = False
+        self.lens_d.copy_(torch.from_numpy(self.paged.lens))
+
+    def place_prompt(self, b, k_layers, v_layers):
+        """Prompt of sequence b: pre-RoPE keys and values [L][nkv][d] (fp32,
+        host) of every layer, written at positions 0..L-1."""
+        torch = _torch()
+        L = int(k_layers[0].shape[0])
+        if L + 1 > self.max_context:
+            raise ValueError("prompt longer than the session's context")
+        self.paged.ensure(b, L)
+        self.paged.lens[b] = L
+        if L == 0:
+            return
+        pos = np.arange(L, dtype=np.int32)
+        pos_d = torch.from_numpy(pos).to(self.device)
+        slots_d = torch.from_numpy(self.paged.slots(b, pos)).to(self.device)
+        for cache, k, v in zip(self.caches, k_layers, v_layers):
+            cache.append(torch.from_numpy(np.ascontiguousarray(k, np.float32)).to(self.device),
+                         torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(self.device), pos_d, slots_d)
+
+    def step(self, tokens, progress=None):
+        """One decode step for every sequence: tokens int32 [batch] (device).
+        Returns the top-1 tokens (device, the next step's input); the logits
+        stay in self.logits.  progress(i, x) runs after block i."""
+        for b in range(self.batch):
+            self.paged.ensure(b, int(self.paged.lens[b]) + 1)
+        if int(self.paged.lens.max()) + 1 > self.max_context:
+            raise RuntimeError("a sequence outgrew the session's context")
+        self._sync_metadata()
+        d = self.dims
+        self.head.embed(tokens, self.x)
+        mpps = self.paged.table.shape[1]
+        for i, (layer, cache) in enumerate(zip(self.layers, self.caches)):
+            F.futx_decode_block(d, layer.c_weights, self.batch, self.x, self.lens_d, self.table_d, mpps,
+                                self.max_context, cache.c_cache, self.workspace, self.ws_bytes)
+            if progress is not None:
+                progress(i, self.x)
+        self.head.lm_head(self.x, self.logits, self.top1)
+        self.paged.lens += 1
+        return self.top1
