@@ -69,12 +69,24 @@ __device__ __forceinline__ bf16x8 widen_word_fast(uint32_t w, NibRegs k) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-__device__ __forceinline__ f16x8 widen_word_exact_f16(uint32_t w) {
+// The same widening to exact fp16 codes: (n | 128-exponent) is the fp16
+// value 128 + n = 136 + code, and one packed fp16 subtraction of 136 per
+// pair leaves the code itself.  The mask and the magic constant sit in
+// registers (nib_regs_f16()), so each pair takes one v_and_or_b32: a VOP3
+// instruction on gfx950 cannot carry literal constants, and with literals
+// the AND and the OR would be two instructions.
+__device__ __forceinline__ NibRegs nib_regs_f16() {
+  NibRegs r{kNibMask, 0x58005800u};
+  asm volatile("" : "+s"(r.mask));  // no instruction: hides the constant
+  asm volatile("" : "+v"(r.magic));
+  return r;
+}
+__device__ __forceinline__ f16x8 widen_word_exact_f16(uint32_t w, NibRegs k) {
   u32x4 r;
-  r.x = (w & kNibMask) | 0x58005800u;
-  r.y = ((w >> 4) & kNibMask) | 0x58005800u;
-  r.z = ((w >> 8) & kNibMask) | 0x58005800u;
-  r.w = (__builtin_amdgcn_alignbit(w, w, 12) & kNibMask) | 0x58005800u;
+  r.x = (w & k.mask) | k.magic;
+  r.y = ((w >> 4) & k.mask) | k.magic;
+  r.z = ((w >> 8) & k.mask) | k.magic;
+  r.w = (__builtin_amdgcn_alignbit(w, w, 12) & k.mask) | k.magic;
   const f16x8 v = __builtin_bit_cast(f16x8, r);
   return v - (f16x8)(_Float16)136.0f;
 }
@@ -116,6 +128,26 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
   return __half2float(__ushort_as_half(h));
+}
+
+// The value held by lane ^ LB (LB = 16 or 32), for every lane, through the
+// gfx950 cross-row swaps instead of an LDS permute.  With both operands x,
+// v_permlane16_swap returns, for each pair of 16-lane rows, x of the even
+// row in its first result and x of the odd row in its second (in every lane
+// of the pair); v_permlane32_swap does the same for the lower and upper 32
+// lanes (checked lane by lane on MI355X).
+template <int LB>
+__device__ __forceinline__ float xor_lanes(float v) {
+  static_assert(LB == 16 || LB == 32, "rows of 16 or halves of 32 lanes");
+  const uint32_t x = __float_as_uint(v);
+  const bool upper = (threadIdx.x & LB) != 0;
+  if constexpr (LB == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return __uint_as_float(upper ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return __uint_as_float(upper ? r[0] : r[1]);
+  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -66,7 +66,7 @@ __host__ __device__ inline GemmLds gemm_lds_layout(int nterms, int B, int krange
 }
 
 struct GemmPlan2 {
-  int nw = 4;  // waves per workgroup (4, 8 or 12), each owning 1 / nw of the K range
+  int nw = 4;  // waves per workgroup (4, 8 or 16), each owning 1 / nw of the K range
   int splits = 1;
   int kb_per_wg = 1;
   int items = 1;

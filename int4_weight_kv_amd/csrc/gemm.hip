@@ -30,13 +30,14 @@
 // Every vector load of the main loop is unconditional: loads complete in
 // order, so the compiler's wait before a use then covers exactly the loads
 // issued before it, and the chunk after the one in use stays in flight.
+#include <algorithm>
 #include <type_traits>
 
 #include "device.h"
 #include "gemm.h"
 
 #ifndef FUTX_GEMM_WIDE_NW
-#define FUTX_GEMM_WIDE_NW 8  // waves per workgroup when items are few (4, 8 or 12)
+#define FUTX_GEMM_WIDE_NW 8  // waves per workgroup when items are few (4 or 8)
 #endif
 #ifndef FUTX_GEMM_OCC
 #define FUTX_GEMM_OCC 3  // workgroups per CU the item split aims at (batch <= 4)
@@ -44,24 +45,29 @@
 #ifndef FUTX_GEMM_OCC_BATCH
 #define FUTX_GEMM_OCC_BATCH 1  // the same for batches above 4
 #endif
+#ifndef FUTX_GEMM_DEEP_MIN_B
+#define FUTX_GEMM_DEEP_MIN_B 5  // smallest batch that uses 16-wave workgroups
+#endif
 #ifndef FUTX_GEMM_WIDE_PCT
 #define FUTX_GEMM_WIDE_PCT 100  // "few": items <= this percentage of the CU count
 #endif
 
 namespace futx {
 
-// Register budget: at most three waves per SIMD (more would make the
-// compiler spill the prologue's staging registers), three for G = 128 and a
-// batch of up to 16, otherwise two or one.
+// Register budget: at most three waves per SIMD for 4- and 8-wave
+// workgroups (more would make the compiler spill the prologue's staging
+// registers); a 16-wave workgroup (one per CU, four waves per SIMD) streams
+// chunks of two K blocks, which keeps it within 128 registers.
 template <int G, int NF, int NR, int NT, bool F32, int EPI, int PAIR, int NW>
-__global__ __launch_bounds__(64 * NW, (NF == 1 && G == 128) ? 2 : 1)
-__attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * NW, (NW < 16 && NF == 1 && G == 128) ? 2 : 1)
+__attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void int4_gemm_kernel(GemmArgs a) {
   constexpr int NTH = 64 * NW;                       // threads per workgroup
   constexpr int NTW = PAIR ? 2 : 1;                  // weight tiles per item (gate + up)
-  constexpr int CHK = (PAIR || NF == 2) ? 4 : 8;     // K blocks per chunk and wave
+  constexpr int CHK = NW == 16 ? 2 : (PAIR || NF == 2) ? 4 : 8;  // K blocks per chunk and wave
   // activation passes held in registers (one L2 round trip each batch of
-  // MAXP); fp32 rows of more than 4 sequences take 8 as well
-  constexpr int MAXP = ((!F32 && NT == 1) || (F32 && NR >= 2)) ? 8 : 4;
+  // MAXP); fp32 rows of more than 4 sequences take 8 as well, except for
+  // gate/up pairs in 16-wave workgroups (register budget)
+  constexpr int MAXP = NW == 16 ? (PAIR ? 4 : 8) : ((!F32 && NT == 1) || (F32 && NR >= 2)) ? 8 : 4;
   extern __shared__ __align__(16) uint8_t s_dyn[];
   // LDS (gemm_lds_layout): activation range [NT][B][row] bf16 | group sums
   // [B][ngr] float2 | group sums of squares [B][ngr] | partials
@@ -140,16 +146,25 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
     return (const uint4*)(a.sc + ((size_t)nt * KB8 + b80 + j) * 16 * SEG) + r;
   };
 
-  // ---- activation staging of this wave's quarter: pass p covers row
-  // p / ppr, elements [(p % ppr) * 512, +512) of the quarter, 8 per lane
+  // ---- activation staging of this wave's quarter: the quarter's rows
+  // [B][qk] are taken as one run of B * qk elements, pass p covering
+  // [p * 512, +512), 8 per lane.  qk is a multiple of 128, so the G / 8
+  // lanes of a weight group always sit in one row.
   const int qk = (q1 - q0) * 128;
-  const int ppr = (qk + 511) >> 9;
-  const int npass = B * ppr;
+  const int nelem = B * qk;
+  const int npass = (nelem + 511) >> 9;
+  // (row, element) of this lane in pass p; lanes past the end read row 0
+  auto act_pos = [&](int p, int& b, int& e) {
+    const int f = p * 512 + lane * 8;
+    const int fc = f < nelem ? f : 0;
+    b = qk ? fc / qk : 0;
+    e = fc - b * qk;
+  };
   using ActRegs = typename std::conditional<F32, float4[2], uint4[NT]>::type;
   auto act_load = [&](int p, ActRegs& r) {  // p < 0 (empty quarter): row 0, a valid address
-    p = p < 0 ? 0 : p;
-    const int b = ppr ? p / ppr : 0, e = (p - b * ppr) * 512 + lane * 8;
-    const size_t src = (size_t)b * a.K + q0 * 128 + (e < qk ? e : 0);
+    int b, e;
+    act_pos(p < 0 ? 0 : p, b, e);
+    const size_t src = (size_t)b * a.K + q0 * 128 + e;
     if constexpr (F32) {
       const float4* q = (const float4*)((const float*)a.act + src);
       r[0] = q[0];
@@ -165,8 +180,9 @@ __attribute__((amdgpu_waves_per_eu(1, 3))) void int4_gemm_kernel(GemmArgs a) {
   // over a dynamically indexed register array (scratch).
   auto act_store = [&](int p, const ActRegs& r, bool valid) {
     if (!valid) return;
-    const int b = p / ppr, e = (p - b * ppr) * 512 + lane * 8;
-    const bool ok = e < qk;
+    int b, e;
+    act_pos(p, b, e);
+    const bool ok = p * 512 + lane * 8 < nelem;
     const int kl = (q0 - kb0) * 128 + e;  // offset in the workgroup's K range
     double gs = 0.0;
     float sq = 0.f;
@@ -474,6 +490,24 @@ static size_t plan_lds(const GemmPlan2& p, int B, int G, int nterms, bool pair) 
   return gemm_lds_bytes(a, nterms, G, pair);
 }
 
+// Items per workgroup for a plan whose splits and waves are set: spread the
+// items evenly over `occ` workgroups per CU, fewer per workgroup while the
+// LDS or the scale registers do not hold them.
+static void plan_items(GemmPlan2& p, int B, int G, int nterms, bool pair, int occ) {
+  const int cus = device_cu_count();
+  const int target = (occ * cus + p.splits - 1) / p.splits;
+  int per = (p.items + target - 1) / target;
+  if (per < 1) per = 1;
+  // scale staging: at most 4 16-byte pieces per thread (registers)
+  const int nkb8 = (p.kb_per_wg + 7) / 8 + 1;
+  auto pieces = [&](int ipw) { return (long)ipw * (pair ? 2 : 1) * nkb8 * 16 * (128 / G); };
+  for (;;) {
+    p.wgs_per_split = (p.items + per - 1) / per;
+    if (per == 1 || (plan_lds(p, B, G, nterms, pair) <= (size_t)kLdsMax && pieces(per) <= 4L * 64 * p.nw)) break;
+    --per;
+  }
+}
+
 GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   GemmPlan2 p;
   const int KB = K / 128;
@@ -488,10 +522,27 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   p.kb_per_wg = (KB + p.splits - 1) / p.splits;
   p.splits = (KB + p.kb_per_wg - 1) / p.kb_per_wg;
   p.items = items;
-  // at most three resident workgroups per CU (the register budget allows
-  // three 4-wave workgroups per CU); items are spread evenly, and a
-  // workgroup's item sums must fit LDS
   const int cus = device_cu_count();
+  // Above 4 sequences every workgroup stages several activation rows, so
+  // the LDS holds one workgroup per CU.  Sixteen waves then share that one
+  // staged copy (four per SIMD, which hides the matrix-core, LDS and
+  // dequantization latencies of one another), each owning at least two K
+  // blocks of every item.
+  // One workgroup per CU: the items are spread over min(items, CUs /
+  // splits) workgroups (the kernel gives each an even share, so item counts
+  // differ by at most one), more while a share does not fit the LDS.
+  if (B >= FUTX_GEMM_DEEP_MIN_B && p.kb_per_wg >= 32) {
+    GemmPlan2 q = p;
+    q.nw = 16;
+    plan_items(q, B, G, nterms, pair, 1);
+    const int even = std::min(items, std::max(1, cus / q.splits));
+    if (even > q.wgs_per_split) {
+      GemmPlan2 r = q;
+      r.wgs_per_split = even;
+      if (plan_lds(r, B, G, nterms, pair) <= plan_lds(q, B, G, nterms, pair)) q = r;
+    }
+    if (plan_lds(q, B, G, nterms, pair) <= (size_t)kLdsMax) return q;
+  }
   // Waves per workgroup: when there are no more items than CUs and K is
   // long, one workgroup per item leaves each CU with few loads in flight, so
   // the item's K range is shared by more waves (measured on MI355X: faster
@@ -502,18 +553,7 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   // where every workgroup stages B activation rows, so fewer workgroups
   // with more items each stage less (measured on MI355X at batch 8: the 8B
   // gate/up projection 32.1 -> 23.4 us; at batch 1 three per CU is best).
-  const int occ = B <= 4 ? FUTX_GEMM_OCC : FUTX_GEMM_OCC_BATCH;
-  const int target = (occ * cus + p.splits - 1) / p.splits;
-  int per = (items + target - 1) / target;
-  if (per < 1) per = 1;
-  // scale staging: at most 4 16-byte pieces per thread (registers)
-  const int nkb8 = (p.kb_per_wg + 7) / 8 + 1;
-  auto pieces = [&](int ipw) { return (long)ipw * (pair ? 2 : 1) * nkb8 * 16 * (128 / G); };
-  for (;;) {
-    p.wgs_per_split = (items + per - 1) / per;
-    if (per == 1 || (plan_lds(p, B, G, nterms, pair) <= (size_t)kLdsMax && pieces(per) <= 4L * 64 * p.nw)) break;
-    --per;
-  }
+  plan_items(p, B, G, nterms, pair, B <= 4 ? FUTX_GEMM_OCC : FUTX_GEMM_OCC_BATCH);
   return p;
 }
 
@@ -526,13 +566,14 @@ hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi
   const bool pair = epi == kEpiSwiglu;
   const dim3 grid(a.splits * a.wgs_per_split), block(64 * a.nw);
   if (a.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
-  if (a.nw != 4 && a.nw != FUTX_GEMM_WIDE_NW) return hipErrorInvalidValue;
+  if (a.nw != 4 && a.nw != FUTX_GEMM_WIDE_NW && a.nw != 16) return hipErrorInvalidValue;
   const size_t lds = gemm_lds_bytes(a, nterms, G, pair);
   if (lds > (size_t)kLdsMax) return hipErrorInvalidValue;
 #define FUTX_G(GG, NF, NR, NT, F32, EPI, PR) \
   do {                                   \
     auto k_ = a.nw == 4 ? int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR, 4> \
-                        : int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR, FUTX_GEMM_WIDE_NW>; \
+              : a.nw == 16 ? int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR, 16> \
+                           : int4_gemm_kernel<GG, NF, NR, NT, F32, EPI, PR, FUTX_GEMM_WIDE_NW>; \
     if (lds > 64 * 1024) {                                                  \
       const hipError_t e_ = hipFuncSetAttribute((const void*)k_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e_ != hipSuccess) return e_;                                      \

@@ -45,6 +45,7 @@ struct AttnArgs {
   int tmax;                    // largest L_b + 1 the plan covers
   float theta;                 // RoPE base
   float scale;                 // 1 / sqrt(D) (set by launch_attn_decode)
+  double inv_freq[64];         // RoPE inverse frequencies theta^(-2i/D), i < D/2 (set by launch_attn_decode)
   KVPtrs kv;
   float* wpart;                // [B][nq][nwg][D + 2] workgroup partials
   float* out_f32;              // [B][nq][D] attention output, or null

@@ -6,6 +6,8 @@
 // MMA operands": INT4 projections whose nibbles are widened to bf16 in
 // registers and fed to the matrix cores, a rotated INT4 KV cache, and
 // split-sequence decode attention.  Operand and cache layouts: layout.h.
+#include <cmath>
+
 #include "device.h"
 #include "gemm.h"
 #include "futx.h"
@@ -91,8 +93,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 // positions keep full accuracy; fp64 sin / cos of the reduced angle in
 // [-pi, pi] then cost no large-argument reduction, and the fp32 results are
 // the correctly rounded values but for rare double-rounding cases.
-__device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float* c, float* s) {
-  const double inv = exp2(-2.0 * (double)i / (double)d * log2((double)theta));
+__device__ __forceinline__ void rope_cs_inv(int pos, double inv, float* c, float* s) {
   const double ang = (double)pos * inv;
   constexpr double kTwoPiHi = 6.28318530717958623200e+00;  // 2 pi rounded to double
   constexpr double kTwoPiLo = 2.44929359829470635445e-16;  // 2 pi - kTwoPiHi
@@ -102,6 +103,10 @@ __device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, floa
   sincos(r, &sn, &cs);  // |r| <= pi: no large-argument reduction left
   *s = (float)sn;
   *c = (float)cs;
+}
+
+__device__ __forceinline__ void rope_cs(int pos, int i, int d, float theta, float* c, float* s) {
+  rope_cs_inv(pos, exp2(-2.0 * (double)i / (double)d * log2((double)theta)), c, s);
 }
 
 // Rotate-half RoPE of one head held as channel c = lane + 64 j, given cos /
@@ -128,16 +133,26 @@ __device__ __forceinline__ void rope_lane(float (&x)[D / 64], int pos, float the
 
 // Normalized Sylvester Hadamard over contiguous blocks of hb channels
 // (hb divides 64, so a block never leaves its 64-lane row).
+template <int HOP, int D>
+__device__ __forceinline__ void fwht_hop(float (&x)[D / 64]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    float o;
+    if constexpr (HOP >= 16) o = xor_lanes<HOP>(x[j]);
+    else o = __shfl_xor(x[j], HOP, 64);
+    x[j] = (lane & HOP) ? o - x[j] : x[j] + o;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void fwht_lane(float (&x)[D / 64], int hb) {
-  const int lane = threadIdx.x & 63;
-  for (int hop = 1; hop < hb; hop <<= 1) {
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-      const float o = __shfl_xor(x[j], hop, 64);
-      x[j] = (lane & hop) ? o - x[j] : x[j] + o;
-    }
-  }
+  if (hb > 1) fwht_hop<1, D>(x);
+  if (hb > 2) fwht_hop<2, D>(x);
+  if (hb > 4) fwht_hop<4, D>(x);
+  if (hb > 8) fwht_hop<8, D>(x);
+  if (hb > 16) fwht_hop<16, D>(x);
+  if (hb > 32) fwht_hop<32, D>(x);
   const float sc = 1.0f / sqrtf((float)hb);
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) x[j] *= sc;
@@ -278,44 +293,16 @@ __device__ __forceinline__ void split_f16(float x, _Float16* hi, _Float16* lo) {
   *lo = (_Float16)(x - (float)*hi);
 }
 
+// Scores are kept in base-2 units (the query scale carries log2 e), so the
+// softmax weights are single exp2 evaluations: exp(x) = 2^(x log2 e).
+constexpr float kLog2e = 1.44269504088896340736f;
+
 // power-of-two exponent k such that m * 2^k lies in [2^(top-1), 2^top)
 __device__ __forceinline__ int range_exp(float m, int top) {
   if (!(m > 0.f)) return 0;
   int e;
   (void)frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
   return top - e;
-}
-
-// Query fragments (B operand of q.k): lane (col, grp) holds query head col
-// of the KV head's group, channels s * 32 + grp * 8 + e in qv[s][e] (fp32).
-// Each head is scaled by an exact power of two into fp16 range and split
-// into hi + lo fp16 operands; returns the inverse scale 2^-kq.
-template <int D>
-__device__ __forceinline__ float q_fragments(const float (&qv)[D / 32][8], f16x8 (&qh)[D / 32],
-                                             f16x8 (&ql)[D / 32]) {
-  float qmax = 0.f;
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qv[s][e]));
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
-  const int kq = range_exp(qmax, 11);
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      _Float16 h0, l0, h1, l1;
-      split_f16(ldexpf(qv[s][e], kq), &h0, &l0);
-      split_f16(ldexpf(qv[s][e + 1], kq), &h1, &l1);
-      hw[e / 2] = pack_h2(h0, h1);
-      lw[e / 2] = pack_h2(l0, l1);
-    }
-    qh[s] = __builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-    ql[s] = __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
-  }
-  return ldexpf(1.0f, -kq);
 }
 
 // A 32-token block of one page and KV head in the attention operand layout
@@ -391,13 +378,15 @@ __device__ __forceinline__ void token_blk(const TokenCodes<D>& t, KvBlk<D>& r) {
 
 // Online-softmax update with one 32-token block starting at token blk
 // (tokens >= t1 masked; at least one token of the block must be < t1):
-// running max m_i and normalizer part l_part of query head col (per lane),
+// running max m_i (base-2 score units) and normalizer part l_part of query
+// head col (per lane),
 // p.v accumulators acc (row 4 grp + r = head, column = channel).
 template <int D>
 __device__ __forceinline__ void compute_blk(int blk, int t1, const KvBlk<D>& rb, const f16x8 (&qh)[D / 32],
                                             const f16x8 (&ql)[D / 32], float zscale, float& m_i, float& l_part,
                                             f32x4 (&acc)[D / 16]) {
   const int lane = threadIdx.x & 63, grp = lane >> 4;
+  const NibRegs nk = nib_regs_f16();
   float ks[2][4], vs[2][4];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -415,7 +404,7 @@ __device__ __forceinline__ void compute_blk(int blk, int t1, const KvBlk<D>& rb,
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      const f16x8 kc = widen_word_exact_f16(rb.kw[u][s]);
+      const f16x8 kc = widen_word_exact_f16(rb.kw[u][s], nk);
       d = mfma16h(kc, qh[s], d);
       d = mfma16h(kc, ql[s], d);
     }
@@ -427,15 +416,15 @@ __device__ __forceinline__ void compute_blk(int blk, int t1, const KvBlk<D>& rb,
       mloc = fmaxf(mloc, z[u][r]);
     }
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+  mloc = fmaxf(mloc, xor_lanes<16>(mloc));
+  mloc = fmaxf(mloc, xor_lanes<32>(mloc));
   const float m_new = fmaxf(m_i, mloc);
-  const float alpha = expf(m_i - m_new);
+  const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
   // exact power-of-two scaling of p * vs (<= max vs) into fp16 range
   float vmax = fmaxf(fmaxf(fmaxf(vs[0][0], vs[0][1]), fmaxf(vs[0][2], vs[0][3])),
                      fmaxf(fmaxf(vs[1][0], vs[1][1]), fmaxf(vs[1][2], vs[1][3])));
-  vmax = fmaxf(vmax, __shfl_xor(vmax, 16, 64));
-  vmax = fmaxf(vmax, __shfl_xor(vmax, 32, 64));
+  vmax = fmaxf(vmax, xor_lanes<16>(vmax));
+  vmax = fmaxf(vmax, xor_lanes<32>(vmax));
   const int kp = range_exp(vmax, 14);
   float psum = 0.f;
   uint32_t phw[4], plw[4];
@@ -443,7 +432,7 @@ __device__ __forceinline__ void compute_blk(int blk, int t1, const KvBlk<D>& rb,
   for (int u = 0; u < 2; ++u) {
 #pragma unroll
     for (int r = 0; r < 4; r += 2) {
-      const float p0 = expf(z[u][r] - m_new), p1 = expf(z[u][r + 1] - m_new);
+      const float p0 = __builtin_amdgcn_exp2f(z[u][r] - m_new), p1 = __builtin_amdgcn_exp2f(z[u][r + 1] - m_new);
       psum += p0 + p1;
       _Float16 h0, l0, h1, l1;
       split_f16(ldexpf(p0 * vs[u][r], kp), &h0, &l0);
@@ -456,50 +445,69 @@ __device__ __forceinline__ void compute_blk(int blk, int t1, const KvBlk<D>& rb,
   m_i = m_new;
   const f16x8 pah = __builtin_bit_cast(f16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
   const f16x8 pal = __builtin_bit_cast(f16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
-  // rescale the p.v accumulators: row 4 (L/16) + r belongs to head 4 grp + r
-  float al[4];
+  // rescale the p.v accumulators: row 4 (L/16) + r belongs to head 4 grp + r.
+  // When no head of the wave moved its running max (alpha = 1 everywhere,
+  // the usual case once the max has settled), the rescale is the identity:
+  // the update fma(dv, pback, acc) is then the same number, and the row
+  // factors are not gathered.
+  const bool moved = __any(alpha != 1.0f);  // wave-uniform
+  float al[4] = {1.f, 1.f, 1.f, 1.f};
+  if (moved) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
+    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * grp + r, 64);
+  }
   const float pback = ldexpf(1.0f, -kp);
 #pragma unroll
   for (int cg = 0; cg < D / 64; ++cg)
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
-      const f16x8 vc = widen_word_exact_f16(word_of(rb.vw[cg], c4));
+      const f16x8 vc = widen_word_exact_f16(word_of(rb.vw[cg], c4), nk);
       f32x4 dv = mfma16h(pah, vc, f32x4{0.f, 0.f, 0.f, 0.f});
       dv = mfma16h(pal, vc, dv);
+      if (moved) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
+        for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(acc[cg * 4 + c4][r], al[r], dv[r] * pback);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[cg * 4 + c4][r] = fmaf(dv[r], pback, acc[cg * 4 + c4][r]);
+      }
     }
 }
 
+// The two 32-token halves of cache page `pg` for KV head h.
+template <int D>
+__device__ __forceinline__ void issue_page(const KVPtrsConst& kv, int pg, int h, KvBlk<D>& r0, KvBlk<D>& r1) {
+  load_blk<D>(kv, pg, 0, h, r0);
+  load_blk<D>(kv, pg, 32, h, r1);
+}
+
 // Online-softmax scan of tokens [t0, t1) of one sequence (block table row
-// bt, t0 page-aligned) against KV head h.  make_q() runs once, after the
-// first page's loads are issued and before its scores, and may fill the
-// query fragments and zscale (their latency then overlaps).  Pages are
-// double-buffered: the loads of page i + 1 are issued before page i is
-// computed; past the last page the loads repeat it (valid addresses) and
-// are not used.
-template <int D, typename MakeQ>
+// bt, t0 page-aligned, page index pg0 = t0 / page size) against KV head h.
+// btv holds the row's entries pg0 + j in lane j (j < 63; lane 63 holds the
+// sequence's first page), so the page of a later step is read from a
+// register, not from memory.  The caller issued the first page into a0 / a1
+// and the second (or the first again) into b0 / b1.  Pages are
+// double-buffered: after page i is computed, the loads of page i + 2 go into
+// its registers; past the last page the loads repeat it (valid addresses)
+// and are not used.
+template <int D>
 __device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x8 (&ql)[D / 32],
-                                           const float& zscale, const int32_t* bt, int t0, int t1, int h,
-                                           int page0, const KVPtrsConst& kv, float& m_i, float& l_part,
-                                           f32x4 (&acc)[D / 16], MakeQ&& make_q) {
-  auto issue_page = [&](int pg, KvBlk<D>& r0, KvBlk<D>& r1) {
-    load_blk<D>(kv, pg, 0, h, r0);
-    load_blk<D>(kv, pg, 32, h, r1);
+                                           const float& zscale, const int32_t* bt, int btv, int pg0, int t0,
+                                           int t1, int h, const KVPtrsConst& kv, float& m_i, float& l_part,
+                                           f32x4 (&acc)[D / 16], KvBlk<D>& a0, KvBlk<D>& a1, KvBlk<D>& b0,
+                                           KvBlk<D>& b1) {
+  auto issue = [&](int pt, KvBlk<D>& r0, KvBlk<D>& r1) {
+    const int pi = min(pt, t1 - 1) / kPageSize;
+    const int j = pi - pg0;  // uniform
+    const int pg = j < 63 ? __builtin_amdgcn_readlane(btv, j) : bt[pi];
+    issue_page<D>(kv, pg, h, r0, r1);
   };
-  auto issue = [&](int pt, KvBlk<D>& r0, KvBlk<D>& r1) { issue_page(bt[min(pt, t1 - 1) / kPageSize], r0, r1); };
   auto consume = [&](int pt, const KvBlk<D>& r0, const KvBlk<D>& r1) {
     compute_blk<D>(pt, t1, r0, qh, ql, zscale, m_i, l_part, acc);
     if (pt + 32 < t1) compute_blk<D>(pt + 32, t1, r1, qh, ql, zscale, m_i, l_part, acc);
   };
-  KvBlk<D> a0, a1, b0, b1;
   int pt = t0;
-  issue_page(page0, a0, a1);  // the first page's table entry was read by the caller (bt[t0 / page size])
-  make_q();  // the query work overlaps the first page's loads
   for (;;) {
-    issue(pt + kPageSize, b0, b1);
     consume(pt, a0, a1);
     pt += kPageSize;
     if (pt >= t1) break;
@@ -507,36 +515,8 @@ __device__ __forceinline__ void split_scan(const f16x8 (&qh)[D / 32], const f16x
     consume(pt, b0, b1);
     pt += kPageSize;
     if (pt >= t1) break;
+    issue(pt + kPageSize, b0, b1);
   }
-}
-
-// One butterfly step (distance HOP channels) of the block Hadamard on query
-// values held as channel s * 32 + grp * 8 + e in qv[s][e] (lane = grp * 16 +
-// col): the same pairing and formula as fwht_lane.
-template <int D, int HOP>
-__device__ __forceinline__ void q_hop(float (&qv)[D / 32][8], int lane) {
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (HOP < 8) {
-        if (!(e & HOP)) {
-          const float x0 = qv[s][e], x1 = qv[s][e + HOP];
-          qv[s][e] = x0 + x1;
-          qv[s][e + HOP] = x0 - x1;
-        }
-      } else if constexpr (HOP < 32) {
-        constexpr int LB = HOP == 8 ? 16 : 32;
-        const float o = __shfl_xor(qv[s][e], LB, 64);
-        qv[s][e] = (lane & LB) ? o - qv[s][e] : qv[s][e] + o;
-      } else if constexpr (D / 32 > 1) {
-        if (!(s & 1)) {
-          const float x0 = qv[s][e], x1 = qv[s + 1][e];
-          qv[s][e] = x0 + x1;
-          qv[s + 1][e] = x0 - x1;
-        }
-      }
-    }
 }
 
 // o (fp32, channel c of query head i) -> the O projection operand: NT bf16
@@ -576,8 +556,10 @@ __device__ __forceinline__ void emit_output(float o, int hb, const AttnArgs& a, 
 //     per token and writes them to the paged cache at slot L_b; the token's
 //     score and value enter the softmax from those same codes in registers
 //     (token_blk), so nothing waits on the cache write;
-//   * the rotated queries (RoPE + block rotation) of the G query heads of
-//     the KV head are recomputed by every wave from the fp32 projection;
+//   * the G query heads of the KV head are rotated (RoPE + block rotation)
+//     once per workgroup, head i by wave i % 4, while the first pages' loads
+//     are in flight, and reach every wave through LDS as fp16 hi / lo
+//     matrix-core fragments;
 //   * split-sequence attention over the cached tokens, the four splits of a
 //     workgroup merged in LDS into one partial (m, l, acc) per head, which
 //     attn_merge_kernel combines across workgroups; when the plan has one
@@ -600,6 +582,10 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   constexpr int MAXG = 16;  // query heads per KV head (matrix-core columns)
   __shared__ float s_m[4][MAXG], s_l[4][MAXG];
+  // rotated queries as fp16 hi / lo (rows padded by 8: the 16 heads' rows
+  // start in different LDS banks) and each head's score scale
+  __shared__ __align__(16) _Float16 s_qhi[MAXG][D + 8], s_qlo[MAXG][D + 8];
+  __shared__ float s_zs[MAXG];
   __shared__ float s_acc[4][MAXG][D];
   const int wg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -611,7 +597,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   const int sp = wg * 4 + wv;
   const int t0 = sp * a.chunk;
   const int32_t* const bt = a.block_table + (size_t)b * a.mpps;
-  const int page0 = bt[min(t0 / kPageSize, a.mpps - 1)];
+  // the block-table entries of this wave's split, one per lane (lane 63: the
+  // sequence's first page, always allocated); clamped into the table row
+  const int pg0 = t0 / kPageSize;
+  const int btv = bt[lane == 63 ? 0 : min(pg0 + lane, a.mpps - 1)];
   const int pos = a.cached_lens[b];  // the new token's position
   const int T = pos + 1;             // tokens attended to
   const size_t obase = ((size_t)b * a.nq + (size_t)h * G) * D;  // output of the group's first head
@@ -635,20 +624,17 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   const bool owner = sp == pos / a.chunk;  // wave-uniform
   const int t1s = owner ? pos : t1;        // cached tokens of the split (the new one comes from registers)
 
-  // 1. loads: the group's queries and the new token's key and value (every
-  //    wave loads them, only the owner uses the key and value: unconditional
-  //    loads keep the memory-counter waits exact)
-  const bool ok = col < G;
-  float qv[D / 32][8];
-  {
-    const float* qrow = row + (size_t)(h * G + (ok ? col : 0)) * D;
+  // 1. loads: this wave's query heads (head wv + 4 k of the group, channel
+  //    lane + 64 j; past the group: head 0 again, ignored) and the new
+  //    token's key and value (every wave loads them, only the owner uses
+  //    them: unconditional loads keep the memory-counter waits exact)
+  constexpr int HPW = MAXG / 4;  // query heads per wave, at most
+  float qx[HPW][D / 64];
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      const float4* qp = (const float4*)(qrow + s * 32 + grp * 8);
-      const float4 x0 = qp[0], x1 = qp[1];
-      qv[s][0] = x0.x; qv[s][1] = x0.y; qv[s][2] = x0.z; qv[s][3] = x0.w;
-      qv[s][4] = x1.x; qv[s][5] = x1.y; qv[s][6] = x1.z; qv[s][7] = x1.w;
-    }
+  for (int k = 0; k < HPW; ++k) {
+    const int i = wv + 4 * k < G ? wv + 4 * k : 0;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) qx[k][j] = row[(size_t)(h * G + i) * D + lane + 64 * j];
   }
   float kx[D / 64], vx[D / 64];
 #pragma unroll
@@ -657,58 +643,74 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
     vx[j] = row[(a.nq + nkv + h) * D + lane + 64 * j];
   }
 
-  // 2. rotated queries as matrix-core fragments, and the owner's new-token
-  //    codes (computed inside the scan while the first page's loads are in
-  //    flight)
-  f16x8 qh[D / 32], ql[D / 32];
-  float zscale = 0.f;
+  // 2. the split's first two pages go out first (a wave with nothing to
+  //    scan reads the sequence's first page and ignores it: unconditional
+  //    loads keep the memory-counter waits exact).  While they are in
+  //    flight, each wave rotates its query heads (RoPE + block rotation, the
+  //    same steps as for the key) and splits them into fp16 hi / lo at the
+  //    head's power-of-two scale; the owner turns the new token into codes.
+  //    The fragments reach every wave through LDS.
+  const bool scan = t0 < t1s;  // wave-uniform
+  KvBlk<D> a0, a1, b0, b1;
+  {
+    const int pfirst = __builtin_amdgcn_readlane(btv, 63);
+    const int p0 = scan ? __builtin_amdgcn_readlane(btv, 0) : pfirst;
+    const int p1 = t0 + kPageSize < t1s ? __builtin_amdgcn_readlane(btv, 1) : p0;
+    issue_page<D>(kvc, p0, h, a0, a1);
+    issue_page<D>(kvc, p1, h, b0, b1);
+  }
+  float cs, sn;  // cos / sin of frequency index lane % (D / 2), shared by the key and the queries
+  rope_cs_inv(pos, a.inv_freq[lane % (D / 2)], &cs, &sn);
   TokenCodes<D> tok;
-  auto make_q = [&]() {
-    float cs, sn;  // cos / sin of frequency index lane % (D / 2), shared by the key and the queries
-    rope_cs(pos, lane % (D / 2), D, a.theta, &cs, &sn);
-    if (owner) {
-      rope_lane_cs<D>(kx, cs, sn);
-      fwht_lane<D>(kx, a.hb);
-      fwht_lane<D>(vx, a.hb);
-      quantize_token<D>(kx, vx, tok);
-    }
-    // rotate-half RoPE: channel c < D/2 (word s) pairs with c + D/2 (word s + D/64)
+  if (owner) {
+    rope_lane_cs<D>(kx, cs, sn);
+    fwht_lane<D>(kx, a.hb);
+    fwht_lane<D>(vx, a.hb);
+    quantize_token<D>(kx, vx, tok);
+  }
 #pragma unroll
-    for (int s = 0; s < D / 64; ++s)
+  for (int k = 0; k < HPW; ++k) {
+    const int i = wv + 4 * k;
+    if (i < G) {  // wave-uniform
+      rope_lane_cs<D>(qx[k], cs, sn);
+      fwht_lane<D>(qx[k], a.hb);
+      float qmax = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int fi = s * 32 + grp * 8 + e;
-        const float c = __shfl(cs, fi, 64), sv = __shfl(sn, fi, 64);
-        const float x0 = qv[s][e], x1 = qv[s + D / 64][e];
-        qv[s][e] = x0 * c - x1 * sv;
-        qv[s + D / 64][e] = x1 * c + x0 * sv;
+      for (int j = 0; j < D / 64; ++j) qmax = fmaxf(qmax, fabsf(qx[k][j]));
+      qmax = wave_max(qmax);
+      const int kq = range_exp(qmax, 11);
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        _Float16 hi, lo;
+        split_f16(ldexpf(qx[k][j], kq), &hi, &lo);
+        s_qhi[i][lane + 64 * j] = hi;
+        s_qlo[i][lane + 64 * j] = lo;
       }
-    // block Hadamard over channel bits: 0..2 in e, 3..4 in grp (lanes 16
-    // and 32 apart), 5 in the word index s; one call per hop, so every
-    // register index is a compile-time constant
-    if (a.hb > 1) q_hop<D, 1>(qv, lane);
-    if (a.hb > 2) q_hop<D, 2>(qv, lane);
-    if (a.hb > 4) q_hop<D, 4>(qv, lane);
-    if (a.hb > 8) q_hop<D, 8>(qv, lane);
-    if (a.hb > 16) q_hop<D, 16>(qv, lane);
-    if (a.hb > 32) q_hop<D, 32>(qv, lane);
-    const float hsc = 1.0f / sqrtf((float)a.hb);
+      if (lane == 0) s_zs[i] = ldexpf(1.0f, -kq) * (a.scale * kLog2e);
+    }
+  }
+  __syncthreads();
+  // matrix-core fragments: lane (grp, col) holds channels 32 s + 8 grp + e
+  // of query head col (zero past the group)
+  const bool ok = col < G;
+  const int qcol = ok ? col : 0;
+  f16x8 qh[D / 32], ql[D / 32];
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[s][e] = ok ? qv[s][e] * hsc : 0.f;
-    zscale = q_fragments<D>(qv, qh, ql) * a.scale;
-  };
+  for (int s = 0; s < D / 32; ++s) {
+    const f16x8 hv = *(const f16x8*)&s_qhi[qcol][s * 32 + grp * 8];
+    const f16x8 lv = *(const f16x8*)&s_qlo[qcol][s * 32 + grp * 8];
+    const f16x8 zero = {};
+    qh[s] = ok ? hv : zero;
+    ql[s] = ok ? lv : zero;
+  }
+  const float zscale = ok ? s_zs[qcol] : 0.f;
 
   // 3. this wave's split: the cached tokens, then (owner) the new token
   float m_i = -INFINITY, l_part = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (t0 < t1s)
-    split_scan<D>(qh, ql, zscale, bt, t0, t1s, h, page0, kvc, m_i, l_part, acc, make_q);
-  else if (owner)
-    make_q();
+  if (scan) split_scan<D>(qh, ql, zscale, bt, btv, pg0, t0, t1s, h, kvc, m_i, l_part, acc, a0, a1, b0, b1);
   if (owner) {
     KvBlk<D> nb;
     token_blk<D>(tok, nb);
@@ -717,8 +719,8 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
     const int slot = bt[pos / kPageSize] * kPageSize + pos % kPageSize;
     store_token<D>(tok, slot, h, a.kv);
   }
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  float l_tot = l_part + xor_lanes<16>(l_part);
+  l_tot += xor_lanes<32>(l_tot);
 
   // 4. the four splits of the workgroup, merged in LDS
   if (grp == 0 && col < G) {
@@ -746,7 +748,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
     acc_c = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // a wave with no tokens has m = -inf: weight 0
-      const float wt = s_m[w][i] == -INFINITY ? 0.f : expf(s_m[w][i] - M);
+      const float wt = s_m[w][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w][i] - M);
       l = fmaf(wt, s_l[w][i], l);
       acc_c = fmaf(wt, s_acc[w][i][c], acc_c);
     }
@@ -833,12 +835,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
       if (ok[u]) mr = fmaxf(mr, mv[u]);
     }
     if (mr == -INFINITY) continue;  // no partial of this phase in the round
-    const float sc = m == -INFINITY ? 0.f : expf(m - mr);
+    const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mr);
     l *= sc;
     a.x *= sc; a.y *= sc; a.z *= sc; a.w *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = ok[u] ? expf(mv[u] - mr) : 0.f;
+      const float w = ok[u] ? __builtin_amdgcn_exp2f(mv[u] - mr) : 0.f;
       if (ok[u]) {  // select: a stale partial never enters, not even times 0
         l = fmaf(w, lv[u], l);
         a.x = fmaf(w, av[u].x, a.x);
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   float o = 0.f, ltot = 0.f;
 #pragma unroll
   for (int p = 0; p < PH; ++p) {
-    const float w = s_m[p] == -INFINITY ? 0.f : expf(s_m[p] - M);
+    const float w = s_m[p] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[p] - M);
     o = fmaf(w, ((const float*)&s_acc[p][c / 4])[c % 4], o);
     ltot = fmaf(w, s_l[p], ltot);
   }
@@ -928,6 +930,9 @@ hipError_t launch_attn_decode(AttnArgs a, int B, int D, const AttnPlan& plan, hi
   a.chunk = plan.chunk;
   a.nwg = (plan.nsplit + 3) / 4;
   a.scale = 1.0f / sqrtf((float)D);
+  // RoPE inverse frequencies theta^(-2i/D) in fp64, the same expression as
+  // the RoPE definition evaluates (the kernels take the angle pos * inv)
+  for (int i = 0; i < 64; ++i) a.inv_freq[i] = i < D / 2 ? std::pow((double)a.theta, -2.0 * i / (double)D) : 0.0;
   const dim3 grid(a.nwg, a.kv.nkv, B);
   if (D == 128)
     attn_decode_kernel<128><<<grid, 256, 0, st>>>(a);
