@@ -168,8 +168,9 @@ futx_status futx_pack_codes_host(const futx_dims* dims, futx_proj proj, const ui
                                  const uint16_t* scales_host, void* packed_host,
                                  void* packed_scales_host);
 
-/* Inverse of the device order (for tests): reads packed_dev / scales_dev and
- * writes canonical bytes [N][K/2] (byte i of a row = code 2i in the low
+/* Inverse of the device order (for tests; the device order is the operand
+ * order in which the dequantized values feed the matrix cores [INT4]): reads
+ * packed_dev / scales_dev and writes canonical bytes [N][K/2] (byte i of a row = code 2i in the low
  * nibble, code 2i+1 in the high nibble, two's complement) and fp16 scales
  * [N][K/w_group] in logical row order (host).  Blocks until done. */
 futx_status futx_unpack_weights(const futx_dims* dims, futx_proj proj, const void* packed_dev,
@@ -179,7 +180,9 @@ futx_status futx_unpack_weights(const futx_dims* dims, futx_proj proj, const voi
 /* ----------------------------------------------------------------- KV cache */
 
 /* Bytes of each code buffer (k_codes and v_codes have the same size) and of
- * each scale buffer for `num_pages` pages. */
+ * each scale buffer for `num_pages` pages of the INT4 cache copy [INT4]: per
+ * page, KV head and token, head_dim / 2 code bytes for keys and as many for
+ * values, and one fp16 scale each. */
 futx_status futx_kv_cache_sizes(const futx_dims* dims, int32_t num_pages, size_t* code_bytes,
                                 size_t* scale_bytes);
 
@@ -197,7 +200,9 @@ futx_status futx_kv_append(const futx_dims* dims, int32_t n_tokens, const float*
 /* ------------------------------------------------------------- decode block */
 
 /* Workspace bytes of futx_decode_block for up to `max_batch` sequences
- * (1..32) of up to `max_context` cached tokens. */
+ * (1..32) of up to `max_context` cached tokens: the decode block of [ABS] at
+ * the batches the pages measure (1..32), its intermediate activations and
+ * attention partials (caller-owned; the library allocates nothing). */
 futx_status futx_decode_workspace_size(const futx_dims* dims, int32_t max_batch,
                                        int32_t max_context, size_t* bytes);
 
@@ -298,8 +303,9 @@ futx_status futx_decode_attention(const futx_dims* dims, int32_t batch, const fl
 
 /* --------------------------------------------------------- full decode step */
 
-/* x[b][:] = fp32(table[tokens[b]][:]) for a bf16 embedding table [vocab][hidden]
- * (dev); tokens int32 [batch] (dev, trusted; out-of-range ids are clamped to
+/* Token embedding of the full decode step whose time the pages report per
+ * token [ABS]: x[b][:] = fp32(table[tokens[b]][:]) for a bf16 embedding table
+ * [vocab][hidden] (dev); tokens int32 [batch] (dev, trusted; out-of-range ids are clamped to
  * [0, vocab)); x fp32 [batch][hidden] (dev).  batch 1..32. */
 futx_status futx_embed(int32_t hidden, int32_t vocab, const uint16_t* table_bf16,
                        const int32_t* tokens, int32_t batch, float* x, void* stream);
