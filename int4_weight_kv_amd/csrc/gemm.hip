@@ -528,12 +528,13 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   // Above 4 sequences every workgroup stages several activation rows, so
   // the LDS holds one workgroup per CU.  Sixteen waves then share that one
   // staged copy (four per SIMD, which hides the matrix-core, LDS and
-  // dequantization latencies of one another), each owning at least two K
-  // blocks of every item.
+  // dequantization latencies of one another), each owning at least one K
+  // block of every item (a 16-block range: measured on MI355X, 8B down
+  // projection at batch 8 18.7 -> 16.8 us, 8B batch 16 down 40 -> 35 us).
   // One workgroup per CU: the items are spread over min(items, CUs /
   // splits) workgroups (the kernel gives each an even share, so item counts
   // differ by at most one), more while a share does not fit the LDS.
-  if (B >= FUTX_GEMM_DEEP_MIN_B && p.kb_per_wg >= 32) {
+  if (B >= FUTX_GEMM_DEEP_MIN_B && p.kb_per_wg >= 16) {
     GemmPlan2 q = p;
     q.nw = 16;
     plan_items(q, B, G, nterms, pair, 1);
@@ -561,6 +562,11 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
 
 bool gemm_fits(int N, int K, int G, int B, int nterms, int epi) {
   const GemmPlan2 p = plan_gemm(N, K, G, B, nterms, epi);
+  // Above 4 sequences a fused epilogue is taken only with 16 waves: a
+  // 4-wave workgroup that fills the LDS alone (one wave per SIMD) is slower
+  // than the 16-wave K split with its finishing kernels (measured on MI355X:
+  // 70B gate/up at batch 8 95 -> 67 us, 8B gate/up at batch 16 50 -> 40 us).
+  if (B >= FUTX_GEMM_DEEP_MIN_B && p.nw != 16) return false;
   return plan_lds(p, B, G, nterms, epi == kEpiSwiglu) <= (size_t)kLdsMax;
 }
 
