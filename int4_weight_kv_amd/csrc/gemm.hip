@@ -244,16 +244,21 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
     const int il = c / cpi;
     const uint8_t* const s_act_c = (const uint8_t*)s_act;
     // A K block past the quarter was loaded from a valid block (its load is
-    // unconditional, see above) and is not computed: the branch is
-    // wave-uniform and holds no memory load, so it costs the loads' waits
-    // nothing (measured on MI355X: the 8B O projection at batch 32 43 -> 25
-    // us, the whole 70B block at batch 32 875 -> 666 us; batches 1-8
-    // unchanged).
+    // unconditional, see above).  Above 8 sequences the K splits leave such
+    // slots in most chunks, and they are skipped: the branch is wave-uniform
+    // and holds no memory load (measured on MI355X: the 8B O projection at
+    // batch 32 43 -> 25 us, the whole 70B block at batch 32 875 -> 666 us).
+    // Up to 8 sequences every wave's share is a whole number of chunks, and
+    // the branch-free form (weight 0) is kept: the branch cost 0.3-0.5 us on
+    // the 8B O and gate/up projections at batch 1.
+    constexpr bool kSkipPast = NR == 4;
 #pragma unroll
     for (int i = 0; i < CHK; ++i) {
       const bool live = cb + i < q1;
-      if (!live) continue;
-      const int kb = cb + i;
+      if constexpr (kSkipPast) {
+        if (!live) continue;
+      }
+      const int kb = live ? cb + i : (q0 < q1 ? q0 : kb0);
 #pragma unroll
       for (int gi = 0; gi < 128 / G; ++gi) {
         f32x4 d[NTW][NF];
@@ -281,7 +286,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
         for (int u = 0; u < NTW; ++u) {
           const uint16_t* st = s_scl + ((size_t)((il * NTW + u) * nkb8 + (kb >> 3) - b80) * 16) * SEG +
                                (kb & 7) * (128 / G) + gi;
-          const float scale = half_bits_to_f32(st[scl_lane]);
+          // read unconditionally (kb is clamped into the staged range), then
+          // select: no branch around the LDS read
+          const float sv = half_bits_to_f32(st[scl_lane]);
+          const float scale = live ? sv : 0.f;
 #pragma unroll
           for (int f = 0; f < NF; ++f)
 #pragma unroll
