@@ -37,7 +37,7 @@
 #include "gemm.h"
 
 #ifndef FUTX_GEMM_WIDE_NW
-#define FUTX_GEMM_WIDE_NW 8  // waves per workgroup when items are few (4 or 8)
+#define FUTX_GEMM_WIDE_NW 16  // waves per workgroup when items are few (4, 8 or 16)
 #endif
 #ifndef FUTX_GEMM_OCC
 #define FUTX_GEMM_OCC 3  // workgroups per CU the item split aims at (batch <= 4)
@@ -557,7 +557,9 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   // Waves per workgroup: when there are no more items than CUs and K is
   // long, one workgroup per item leaves each CU with few loads in flight, so
   // the item's K range is shared by more waves (measured on MI355X: faster
-  // for the 8B down projection, K = 14336; slower for K = 4096).
+  // for the 8B down projection, K = 14336; slower for K = 4096).  Sixteen
+  // waves (chunks of two K blocks) beat eight there: 8B down at batch 4
+  // 15.8 -> 14.5 us, batch 1 equal.
   p.nw = 4;
   if (p.splits == 1 && (long)items * 100 <= (long)cus * FUTX_GEMM_WIDE_PCT && KB >= 64) p.nw = FUTX_GEMM_WIDE_NW;
   // Workgroups per CU aimed at: three for up to 4 sequences; one above,
