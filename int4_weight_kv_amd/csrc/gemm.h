@@ -38,6 +38,7 @@ struct GemmArgs {
   int items;             // 16-row tiles (gate/up pairs for kEpiSwiglu)
   int wgs_per_split;     // workgroups per split, each with a run of items
   int nw;                // waves per workgroup
+  int ntiles;            // batch tiles (rows split evenly; 0 or 1: one tile)
   float eps;             // RMSNorm epsilon
   const float* resid;    // kEpiResid
   float* out;            // kEpiPartial / kEpiRms / kEpiResid
@@ -71,6 +72,7 @@ struct GemmPlan2 {
   int kb_per_wg = 1;
   int items = 1;
   int wgs_per_split = 1;
+  int ntiles = 1;  // batch tiles, each planned as its own batch on CUs / ntiles
 };
 
 // Work plan: K splits (only kEpiPartial splits K, until the activation
@@ -89,6 +91,7 @@ inline void apply_plan(GemmArgs& a, const GemmPlan2& p) {
   a.items = p.items;
   a.wgs_per_split = p.wgs_per_split;
   a.nw = p.nw;
+  a.ntiles = p.ntiles;
 }
 
 }  // namespace futx

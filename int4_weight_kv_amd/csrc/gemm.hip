@@ -46,7 +46,7 @@
 #define FUTX_GEMM_OCC_BATCH 1  // the same for batches above 4
 #endif
 #ifndef FUTX_GEMM_DEEP_MIN_B
-#define FUTX_GEMM_DEEP_MIN_B 5  // smallest batch that uses 16-wave workgroups
+#define FUTX_GEMM_DEEP_MIN_B 5  // smallest batch whose fused epilogues need 16-wave workgroups
 #endif
 #ifndef FUTX_GEMM_WIDE_PCT
 #define FUTX_GEMM_WIDE_PCT 100  // "few": items <= this percentage of the CU count
@@ -76,9 +76,22 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   const int tid = threadIdx.x, lane = tid & 63;
   const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (0..NW-1), scalar
   const int col = lane & 15, grp = lane >> 4;
-  const int B = a.B;
+  // Batch tiles: workgroup w of tile t runs as block ((w / 8) * ntiles + t)
+  // * 8 + w % 8.  Blocks go to the 8 XCDs in turn, so the tiles of one item
+  // run sit on one XCD at the same time and read the weights through its L2
+  // (one HBM read).  Blocks past the plan (grid padding) leave at once.
+  int wgi = blockIdx.x, bt = 0;
+  const int ntl = a.ntiles > 1 ? a.ntiles : 1;
+  if (ntl > 1) {
+    const int r = wgi >> 3;
+    bt = r % ntl;
+    wgi = (r / ntl) * 8 + (wgi & 7);
+  }
+  if (wgi >= a.splits * a.wgs_per_split) return;
+  const int b0 = __builtin_amdgcn_readfirstlane(bt * a.B / ntl);                // first row of the tile
+  const int B = __builtin_amdgcn_readfirstlane((bt + 1) * a.B / ntl) - b0;       // rows of the tile
   const int KB = a.K >> 7;
-  const int split = blockIdx.x / a.wgs_per_split, wj = blockIdx.x - split * a.wgs_per_split;
+  const int split = wgi / a.wgs_per_split, wj = wgi - split * a.wgs_per_split;
   const int kb0 = split * a.kb_per_wg, kb1 = min(kb0 + a.kb_per_wg, KB);
   const int krange = kb1 - kb0;
   const int it0 = (int)((long)wj * a.items / a.wgs_per_split);
@@ -113,7 +126,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   if constexpr (EPI == kEpiResid) {
     const int idx = min(tid, (it1 - it0) * B * 16 - 1);
     const int il = idx / (B * 16), rem = idx - il * B * 16;
-    resid_pf = a.resid[(size_t)(rem >> 4) * a.N + (it0 + il) * 16 + (rem & 15)];
+    resid_pf = a.resid[(size_t)(b0 + (rem >> 4)) * a.N + (it0 + il) * 16 + (rem & 15)];
   }
 
   // ---- weights: the main loop issues weight loads only (scales come from LDS)
@@ -164,7 +177,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   auto act_load = [&](int p, ActRegs& r) {  // p < 0 (empty quarter): row 0, a valid address
     int b, e;
     act_pos(p < 0 ? 0 : p, b, e);
-    const size_t src = (size_t)b * a.K + q0 * 128 + e;
+    const size_t src = (size_t)(b0 + b) * a.K + q0 * 128 + e;
     if constexpr (F32) {
       const float4* q = (const float4*)((const float*)a.act + src);
       r[0] = q[0];
@@ -455,16 +468,16 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
     const int n = (it0 + il) * 16 + cc;  // physical row (non-pair) / logical column (pair)
     const float o = s_out[((il * NTW) * B + tok) * 16 + cc];
     if constexpr (EPI == kEpiPartial) {
-      a.out[((size_t)split * B + tok) * a.N + n] = o;
+      a.out[((size_t)split * a.B + b0 + tok) * a.N + n] = o;
     } else if constexpr (EPI == kEpiRms) {
-      a.out[(size_t)tok * a.N + n] = o * (1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps));
+      a.out[(size_t)(b0 + tok) * a.N + n] = o * (1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps));
     } else if constexpr (EPI == kEpiResid) {
-      const float rv = idx == tid ? resid_pf : a.resid[(size_t)tok * a.N + n];
-      a.out[(size_t)tok * a.N + n] = rv + o;
+      const float rv = idx == tid ? resid_pf : a.resid[(size_t)(b0 + tok) * a.N + n];
+      a.out[(size_t)(b0 + tok) * a.N + n] = rv + o;
     } else {  // kEpiSwiglu: u = 0 gate rows, u = 1 up rows of logical column n
       const float invr = 1.0f / sqrtf(s_ss[tok] / (float)a.K + a.eps);
       const float g = o * invr, up = s_out[((il * NTW + PAIR) * B + tok) * 16 + cc] * invr;
-      a.out_bf16[(size_t)tok * a.inter + n] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * up);
+      a.out_bf16[(size_t)(b0 + tok) * a.inter + n] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * up);
     }
   }
 }
@@ -481,13 +494,20 @@ int device_cu_count() {
   return cached[dev];
 }
 
+// rows of the largest batch tile
+static int tile_rows(const GemmArgs& a) {
+  const int nt = a.ntiles > 1 ? a.ntiles : 1;
+  return (a.B + nt - 1) / nt;
+}
+
 size_t gemm_lds_bytes(const GemmArgs& a, int nterms, int G, bool pair) {
   const int krange = a.kb_per_wg;
-  const int nf = a.B <= 16 ? 1 : 2;
-  const int nr = a.B <= 4 ? 1 : a.B <= 8 ? 2 : 4;
+  const int bt = tile_rows(a);
+  const int nf = bt <= 16 ? 1 : 2;
+  const int nr = bt <= 4 ? 1 : bt <= 8 ? 2 : 4;
   const int items_wg = (a.items + a.wgs_per_split - 1) / a.wgs_per_split;
   const int nkb8 = (krange + 7) / 8 + 1;  // a K range not aligned to 8 blocks spans one more
-  return gemm_lds_layout(nterms, a.B, krange, G, pair ? 2 : 1, nf * nr, items_wg, nkb8, a.nw).total;
+  return gemm_lds_layout(nterms, bt, krange, G, pair ? 2 : 1, nf * nr, items_wg, nkb8, a.nw).total;
 }
 
 static size_t plan_lds(const GemmPlan2& p, int B, int G, int nterms, bool pair) {
@@ -503,8 +523,7 @@ static size_t plan_lds(const GemmPlan2& p, int B, int G, int nterms, bool pair) 
 // Items per workgroup for a plan whose splits and waves are set: spread the
 // items evenly over `occ` workgroups per CU, fewer per workgroup while the
 // LDS or the scale registers do not hold them.
-static void plan_items(GemmPlan2& p, int B, int G, int nterms, bool pair, int occ) {
-  const int cus = device_cu_count();
+static void plan_items(GemmPlan2& p, int B, int G, int nterms, bool pair, int occ, int cus) {
   const int target = (occ * cus + p.splits - 1) / p.splits;
   int per = (p.items + target - 1) / target;
   if (per < 1) per = 1;
@@ -518,7 +537,8 @@ static void plan_items(GemmPlan2& p, int B, int G, int nterms, bool pair, int oc
   }
 }
 
-GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
+// Plan of one batch tile of B rows on `cus` CUs.
+static GemmPlan2 plan_tile(int N, int K, int G, int B, int nterms, int epi, int cus) {
   GemmPlan2 p;
   const int KB = K / 128;
   const bool pair = epi == kEpiSwiglu;
@@ -532,7 +552,6 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   p.kb_per_wg = (KB + p.splits - 1) / p.splits;
   p.splits = (KB + p.kb_per_wg - 1) / p.kb_per_wg;
   p.items = items;
-  const int cus = device_cu_count();
   // Above 4 sequences every workgroup stages several activation rows, so
   // the LDS holds one workgroup per CU.  Sixteen waves then share that one
   // staged copy (four per SIMD, which hides the matrix-core, LDS and
@@ -542,17 +561,44 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   // One workgroup per CU: the items are spread over min(items, CUs /
   // splits) workgroups (the kernel gives each an even share, so item counts
   // differ by at most one), more while a share does not fit the LDS.
-  if (B >= FUTX_GEMM_DEEP_MIN_B && p.kb_per_wg >= 16) {
-    GemmPlan2 q = p;
-    q.nw = 16;
-    plan_items(q, B, G, nterms, pair, 1);
-    const int even = std::min(items, std::max(1, cus / q.splits));
-    if (even > q.wgs_per_split) {
-      GemmPlan2 r = q;
-      r.wgs_per_split = even;
-      if (plan_lds(r, B, G, nterms, pair) <= plan_lds(q, B, G, nterms, pair)) q = r;
+  // Below 5 sequences the same shape wins for large projections, where the
+  // 4-wave workgroups staging B activation rows each leave one or two
+  // workgroups per CU (measured on MI355X, 70B: O at batch 4 25.8 -> 15.6
+  // us, gate/up at batch 1 53 -> 45 us, down at batch 2 45 -> 28 us), but
+  // not for small ones at small batch (8B O at batch 2 6.4 -> 7.9 us).  The
+  // weight bytes per CU above which it is taken fall with the batch.
+  const long wcu = (long)N * K / 2 / cus;
+  const bool deep = B >= 4 || (B >= 2 && wcu >= (128L << 10)) || (KB >= 64 && wcu >= (256L << 10));
+  // A plan that needs more workgroups than CUs (the items of a share do not
+  // fit the LDS) runs a second, partial round; K splits beyond the LDS
+  // minimum (kEpiPartial) shrink the staged range until one round holds
+  // the items (measured on MI355X, 70B at batch 16 in two 8-row tiles:
+  // ...).  Without such a split the first plan that fits is kept.
+  if (deep && p.kb_per_wg >= 16) {
+    GemmPlan2 first;
+    bool have = false;
+    for (GemmPlan2 sp = p;;) {
+      GemmPlan2 q = sp;
+      q.nw = 16;
+      plan_items(q, B, G, nterms, pair, 1, cus);
+      const int even = std::min(items, std::max(1, cus / q.splits));
+      if (even > q.wgs_per_split) {
+        GemmPlan2 r = q;
+        r.wgs_per_split = even;
+        if (plan_lds(r, B, G, nterms, pair) <= plan_lds(q, B, G, nterms, pair)) q = r;
+      }
+      if (plan_lds(q, B, G, nterms, pair) <= (size_t)kLdsMax) {
+        if (q.splits * q.wgs_per_split <= cus) return q;
+        if (!have) first = q, have = true;
+      }
+      if (epi != kEpiPartial) break;
+      int ns = sp.splits + 1, kb = 0;
+      while (ns <= KB && (kb = (KB + ns - 1) / ns) == sp.kb_per_wg) ++ns;
+      if (ns > KB || kb < 16) break;
+      sp.kb_per_wg = kb;
+      sp.splits = (KB + kb - 1) / kb;
     }
-    if (plan_lds(q, B, G, nterms, pair) <= (size_t)kLdsMax) return q;
+    if (have) return first;
   }
   // Waves per workgroup: when there are no more items than CUs and K is
   // long, one workgroup per item leaves each CU with few loads in flight, so
@@ -566,12 +612,23 @@ GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
   // where every workgroup stages B activation rows, so fewer workgroups
   // with more items each stage less (measured on MI355X at batch 8: the 8B
   // gate/up projection 32.1 -> 23.4 us; at batch 1 three per CU is best).
-  plan_items(p, B, G, nterms, pair, B <= 4 ? FUTX_GEMM_OCC : FUTX_GEMM_OCC_BATCH);
+  plan_items(p, B, G, nterms, pair, B <= 4 ? FUTX_GEMM_OCC : FUTX_GEMM_OCC_BATCH, cus);
   return p;
 }
 
-bool gemm_fits(int N, int K, int G, int B, int nterms, int epi) {
-  const GemmPlan2 p = plan_gemm(N, K, G, B, nterms, epi);
+static GemmPlan2 plan_tiled(int N, int K, int G, int B, int nterms, int epi, int nt) {
+  const int cus = device_cu_count();
+  GemmPlan2 p = plan_tile(N, K, G, (B + nt - 1) / nt, nterms, epi, std::max(1, cus / nt));
+  p.ntiles = nt;
+  return p;
+}
+
+// Whether a plan of a fused epilogue applies.
+static bool tile_fits(const GemmPlan2& p, int B, int G, int nterms, int epi) {
+  B = (B + p.ntiles - 1) / p.ntiles;  // rows of a tile
+  // a 16-wave plan in more than one round: the K split (one round) is
+  // faster (measured on MI355X, 70B down at batch 8 57 -> 35 us)
+  if (p.nw == 16 && (long)p.ntiles * p.splits * p.wgs_per_split > device_cu_count()) return false;
   // Above 4 sequences a fused epilogue is taken only with 16 waves: a
   // 4-wave workgroup that fills the LDS alone (one wave per SIMD) is slower
   // than the 16-wave K split with its finishing kernels (measured on MI355X:
@@ -580,9 +637,101 @@ bool gemm_fits(int N, int K, int G, int B, int nterms, int epi) {
   return plan_lds(p, B, G, nterms, epi == kEpiSwiglu) <= (size_t)kLdsMax;
 }
 
+// Batch tiles above 8 sequences.  Every tile streams all the weights (from
+// the L2 of its XCD after the first), so tiling trades weight-block slots
+// for a smaller staged activation: fewer K splits and empty chunk slots.
+// The plans compared here have one workgroup per CU; the estimate is the
+// critical path per CU in weight-block slots (rounds x items per workgroup x
+// slots per item, empty ones included: their loads are issued), plus a
+// fixed charge for the finishing kernels of a K split; ties go to fewer
+// tiles.  Measured on MI355X against one tile: 8B at batch 16 in 8-row
+// tiles 152 -> 113 us per block; 70B down at batch 16 78 -> 56 us, while
+// 70B O and gate/up at batch 16 stay in one tile (31.6 vs 38.6 and 119.7
+// vs 146.6 us in two), as the estimate has it.
+constexpr double kSplitCharge = 32.0;
+
+static double plan_cost(const GemmPlan2& p, int B, bool pair) {
+  const int bt = (B + p.ntiles - 1) / p.ntiles;
+  const int ntw = pair ? 2 : 1;
+  const long ipw = (p.items + p.wgs_per_split - 1) / p.wgs_per_split;
+  const int kbq = (p.kb_per_wg + p.nw - 1) / p.nw;
+  const int chk = p.nw == 16 ? 2 : (pair || bt > 16) ? 4 : 8;
+  const long slots = (long)(kbq + chk - 1) / chk * chk * p.nw;
+  const long cus = device_cu_count();
+  const long rounds = ((long)p.ntiles * p.splits * p.wgs_per_split + cus - 1) / cus;
+  return (double)(rounds * ipw * ntw * slots);
+}
+
+// Tile counts compared: tiles of at most 16 and at most 8 rows (one tile up
+// to 8 sequences).  Tiles of more than 16 rows are not used: with two
+// matrix-core fragments per weight block they measured slower than 8-row
+// tiles for every projection (8B at batch 32: 247 vs 162 us per block).
+static int tile_counts(int B, int (&nt)[3]) {
+  int n = 0;
+  for (int rows : {16, 8}) {
+    const int t = (B + rows - 1) / rows;
+    if (n == 0 || t != nt[n - 1]) nt[n++] = t;
+  }
+  return n;
+}
+
+static GemmPlan2 best_partial(int N, int K, int G, int B, int nterms, double* cost) {
+  int nt[3];
+  const int n = tile_counts(B, nt);
+  GemmPlan2 best;
+  double bc = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const GemmPlan2 q = plan_tiled(N, K, G, B, nterms, kEpiPartial, nt[i]);
+    const double c = plan_cost(q, B, false) + kSplitCharge;
+    if (i == 0 || c < bc) best = q, bc = c;
+  }
+  if (cost) *cost = bc;
+  return best;
+}
+
+// Plan of an epilogue: fused (one kernel) or, when that does not fit or is
+// estimated slower, the K-split partial plan whose sums separate kernels
+// finish.  Up to 8 sequences: one tile, fused whenever it fits.
+static GemmPlan2 choose(int N, int K, int G, int B, int nterms, int epi, bool* fused) {
+  *fused = false;
+  if (epi == kEpiPartial) return best_partial(N, K, G, B, nterms, nullptr);
+  int nt[3];
+  const int n = tile_counts(B, nt);
+  GemmPlan2 best;
+  double bc = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const GemmPlan2 f = plan_tiled(N, K, G, B, nterms, epi, nt[i]);
+    if (!tile_fits(f, B, G, nterms, epi)) continue;
+    const double c = plan_cost(f, B, epi == kEpiSwiglu);
+    if (!*fused || c < bc) best = f, bc = c, *fused = true;
+  }
+  if (*fused && B <= 8) return best;
+  double pc;
+  const GemmPlan2 q = best_partial(N, K, G, B, nterms, &pc);
+  if (!*fused || pc < bc) {
+    *fused = false;
+    return q;
+  }
+  return best;
+}
+
+GemmPlan2 plan_gemm(int N, int K, int G, int B, int nterms, int epi) {
+  bool fused;
+  return choose(N, K, G, B, nterms, epi, &fused);
+}
+
+bool gemm_fits(int N, int K, int G, int B, int nterms, int epi) {
+  bool fused;
+  choose(N, K, G, B, nterms, epi, &fused);
+  return fused;
+}
+
 hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi, hipStream_t st) {
   const bool pair = epi == kEpiSwiglu;
-  const dim3 grid(a.splits * a.wgs_per_split), block(64 * a.nw);
+  const int ntl = a.ntiles > 1 ? a.ntiles : 1, bt = tile_rows(a);
+  const int nwg = a.splits * a.wgs_per_split;
+  const dim3 grid(ntl > 1 ? (nwg + 7) / 8 * 8 * ntl : nwg), block(64 * a.nw);
+  if (ntl > a.B) return hipErrorInvalidValue;
   if (a.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
   if (a.nw != 4 && a.nw != FUTX_GEMM_WIDE_NW && a.nw != 16) return hipErrorInvalidValue;
   const size_t lds = gemm_lds_bytes(a, nterms, G, pair);
@@ -600,9 +749,9 @@ hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi
   } while (0)
 #define FUTX_NF(GG, NT, F32, EPI, PR) \
   do {                                  \
-    if (a.B <= 4) FUTX_G(GG, 1, 1, NT, F32, EPI, PR);                  \
-    else if (a.B <= 8) FUTX_G(GG, 1, 2, NT, F32, EPI, PR);             \
-    else if (a.B <= 16) FUTX_G(GG, 1, 4, NT, F32, EPI, PR);            \
+    if (bt <= 4) FUTX_G(GG, 1, 1, NT, F32, EPI, PR);                   \
+    else if (bt <= 8) FUTX_G(GG, 1, 2, NT, F32, EPI, PR);              \
+    else if (bt <= 16) FUTX_G(GG, 1, 4, NT, F32, EPI, PR);             \
     else FUTX_G(GG, 2, 4, NT, F32, EPI, PR);                           \
   } while (0)
 #define FUTX_GRP(NT, F32, EPI, PR)                                        \

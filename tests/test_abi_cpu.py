@@ -97,6 +97,19 @@ def test_lm_head_workspace_and_validation(fx):
     assert e.value.status == fx.FUTX_E_ARG
 
 
+def test_noalloc_scratch_bounds(fx):
+    """The static buffer of futx_decode_block_noalloc (72 MiB, include/futx.h)
+    holds the 70B-shape block at batch 32, and the request the GPU rejection
+    test makes (with placeholder buffers) needs more than twice that: that
+    test relies on the call being refused before any launch."""
+    scratch = 72 << 20
+    for mc in (4097, 8193, 131073):
+        assert fx.futx_decode_workspace_size(W.llama70b(32).dims, 32, mc) <= scratch
+        assert fx.futx_decode_workspace_size(W.LLAMA8B, 32, mc) <= scratch
+    big = W.Dims(16384, 64, 8, 128, 229376, 128, 64)
+    assert fx.futx_decode_workspace_size(big, 32, 9) > 2 * scratch
+
+
 def test_sizes(fx):
     pb, sb = fx.futx_packed_sizes(W.LLAMA8B, "gateup")
     assert pb == 2 * 14336 * 4096 // 2 and sb == 2 * 14336 * 32 * 2

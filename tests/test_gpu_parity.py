@@ -165,35 +165,56 @@ def test_kv_append_rotation_ablation(F, DB):
 # ---------------------------------------------------------------- projections
 
 
+def _check_int4_linear(F, DB, shape, d, proj, m, g, batch, r):
+    n, kk = m.shape
+    act = W.to_bf16_values(r.standard_normal((batch, kk)).astype(np.float32))
+    abits = (act.view(np.uint32) >> 16).astype(np.uint16)
+    pp = DB.pack_projection(d, proj, m, g)
+    ws_bytes = F.futx_decode_workspace_size(d, batch, 1)
+    ws = DB.device_buffer(ws_bytes)
+    out = torch.empty((batch, n), dtype=torch.float32, device="cuda")
+    say("int4_linear", shape, proj, "batch", batch)
+    F.futx_int4_linear(d, proj, (pp.packed, pp.scales), batch, torch.from_numpy(abits).cuda(), out, ws,
+                       ws_bytes)
+    torch.cuda.synchronize()
+    folded = m if g is None else oracle.fold_gain(m, g)
+    q, s = oracle.quantize_weight_rtn(folded, d.w_group)
+    ref = act.astype(np.float64) @ oracle.dequant_weight(q, s, d.w_group).T
+    err = np.max(np.abs(out.cpu().numpy() - ref))
+    say("  max err %.3g  (max|ref| %.3g)" % (err, np.max(np.abs(ref))))
+    # fp32 accumulation over K inputs: far below the block tolerance
+    assert err <= 1e-5 * np.max(np.abs(ref)) * np.sqrt(kk / 128) + 1e-6, (proj, err)
+
+
 @pytest.mark.parametrize("shape", ["tiny", "8b"])
-@pytest.mark.parametrize("batch", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 16, 17, 32])
 def test_int4_linear(F, DB, shape, batch):
+    # batches 1-5 cross the planner's workgroup shapes: 4-wave workgroups, and
+    # 16-wave ones for the large projections from batch 2 and all from batch 4
     wl = W.tiny() if shape == "tiny" else W.llama8b()
-    d = wl.dims
     w = W.block_weights(wl, 0)
     r = np.random.default_rng(23 + batch)
     for proj, m, g in (("qkv", w["wqkv"], w["gain_attn"]), ("o", w["wo"], None),
                        ("gateup", np.concatenate([w["wgate"], w["wup"]]), w["gain_ffn"]), ("down", w["wdown"], None)):
-        if shape == "8b" and proj in ("qkv", "o") and batch not in (1, 32):
+        if shape == "8b" and proj in ("qkv", "o") and batch not in (1, 2, 4, 32):
             continue
-        n, kk = m.shape
-        act = W.to_bf16_values(r.standard_normal((batch, kk)).astype(np.float32))
-        abits = (act.view(np.uint32) >> 16).astype(np.uint16)
-        pp = DB.pack_projection(d, proj, m, g)
-        ws_bytes = F.futx_decode_workspace_size(d, batch, 1)
-        ws = DB.device_buffer(ws_bytes)
-        out = torch.empty((batch, n), dtype=torch.float32, device="cuda")
-        say("int4_linear", shape, proj, "batch", batch)
-        F.futx_int4_linear(d, proj, (pp.packed, pp.scales), batch, torch.from_numpy(abits).cuda(), out, ws,
-                           ws_bytes)
-        torch.cuda.synchronize()
-        folded = m if g is None else oracle.fold_gain(m, g)
-        q, s = oracle.quantize_weight_rtn(folded, d.w_group)
-        ref = act.astype(np.float64) @ oracle.dequant_weight(q, s, d.w_group).T
-        err = np.max(np.abs(out.cpu().numpy() - ref))
-        say("  max err %.3g  (max|ref| %.3g)" % (err, np.max(np.abs(ref))))
-        # fp32 accumulation over K inputs: far below the block tolerance
-        assert err <= 1e-5 * np.max(np.abs(ref)) * np.sqrt(kk / 128) + 1e-6, (proj, err)
+        _check_int4_linear(F, DB, shape, wl.dims, proj, m, g, batch, r)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("batch", [2, 3])
+def test_int4_linear_70b(F, DB, batch):
+    """Llama-3-70B-shape QKV, O and down projections at batches 2 and 3, where
+    they take 16-wave workgroups (down at batch 3 as a K split with its
+    finishing kernel)."""
+    d = W.llama70b(batch).dims
+    r = np.random.default_rng(31 + batch)
+    nq_d = d.n_heads * d.head_dim
+    for proj, shape, gained in (("qkv", (d.n_qkv, d.hidden), True), ("o", (d.hidden, nq_d), False),
+                                ("down", (d.hidden, d.intermediate), False)):
+        m = (r.standard_normal(shape) * 0.02).astype(np.float32)
+        g = r.uniform(0.5, 1.5, d.hidden).astype(np.float32) if gained else None
+        _check_int4_linear(F, DB, "70b", d, proj, m, g, batch, r)
 
 
 def test_int4_linear_external_codes(F, DB):
@@ -403,8 +424,9 @@ def test_block_tiny():
     np.testing.assert_array_equal(V[0], oc.v_codes[L])
 
 
-@pytest.mark.parametrize("batch,lens", [(3, "fixed:0"), (4, "uniform:1:200")])
+@pytest.mark.parametrize("batch,lens", [(3, "fixed:0"), (4, "uniform:1:200"), (17, "uniform:1:200")])
 def test_block_tiny_ragged(batch, lens):
+    # batch 17: the projections run in batch tiles of unequal row counts
     wl = W.Workload(f"tiny-ragged-b{batch}-{lens}", W.TINY, batch, lens)
     _check_block(BlockCase(wl))
 
@@ -413,8 +435,10 @@ def test_block_8b():
     _check_block(BlockCase(W.llama8b()), reps=1)
 
 
-@pytest.mark.parametrize("batch", [1, 4, 8, 16, 32])
+@pytest.mark.parametrize("batch", [1, 4, 8, 16, 17, 32])
 def test_block_8b_ragged_outliers(batch):
+    # batches 16, 17 and 32 run the projections in batch tiles (17: tiles of
+    # unequal row counts)
     # batch 32 (split-K projections and their reduce kernels) runs twice and
     # must repeat bit for bit
     _check_block(BlockCase(W.llama8b_ragged(batch)), reps=2 if batch == 32 else 1)
