@@ -572,8 +572,9 @@ static GemmPlan2 plan_tile(int N, int K, int G, int B, int nterms, int epi, int 
   // A plan that needs more workgroups than CUs (the items of a share do not
   // fit the LDS) runs a second, partial round; K splits beyond the LDS
   // minimum (kEpiPartial) shrink the staged range until one round holds
-  // the items (measured on MI355X, 70B at batch 16 in two 8-row tiles:
-  // ...).  Without such a split the first plan that fits is kept.
+  // the items (measured on MI355X: 70B down at batch 8 in 8 instead of 7
+  // splits 57 -> 35 us, at batch 16 in two 8-row tiles 92 -> 56 us).
+  // Without such a split the first plan that fits is kept.
   if (deep && p.kb_per_wg >= 16) {
     GemmPlan2 first;
     bool have = false;
