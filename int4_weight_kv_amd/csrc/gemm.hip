@@ -65,9 +65,10 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   constexpr int NTW = PAIR ? 2 : 1;                  // weight tiles per item (gate + up)
   constexpr int CHK = NW == 16 ? 2 : (PAIR || NF == 2) ? 4 : 8;  // K blocks per chunk and wave
   // activation passes held in registers (one L2 round trip each batch of
-  // MAXP); fp32 rows of more than 4 sequences take 8 as well, except for
-  // gate/up pairs in 16-wave workgroups (register budget)
-  constexpr int MAXP = NW == 16 ? (PAIR ? 4 : 8) : ((!F32 && NT == 1) || (F32 && NR >= 2)) ? 8 : 4;
+  // MAXP); fp32 rows of more than 4 sequences take 8 as well, except in
+  // 16-wave workgroups (register budget; two round trips of 4 measured no
+  // slower there)
+  constexpr int MAXP = NW == 16 ? 4 : ((!F32 && NT == 1) || (F32 && NR >= 2)) ? 8 : 4;
   extern __shared__ __align__(16) uint8_t s_dyn[];
   // LDS (gemm_lds_layout): activation range [NT][B][row] bf16 | group sums
   // [B][ngr] float2 | group sums of squares [B][ngr] | partials
@@ -365,7 +366,12 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   // first, then the first weight chunk(s); staging then waits for the
   // activation only.  Both staging paths end with only weight loads in
   // flight.
-  auto prologue = [&](auto two_chunks) {
+  auto prologue = [&](auto two_chunks, auto maxp) {
+    // passes held in registers: the smallest of 1, 2, 4 and MAXP that
+    // covers the wave's passes, so that no load repeats a pass (such loads
+    // still occupy the CU's vector-memory path, which bounds the prologue:
+    // measured on MI355X, 8B block at batch 8 88 -> 84 us, 70B 191 -> 185)
+    constexpr int MP = decltype(maxp)::value;
     // scales first (oldest loads: waiting for them does not wait for
     // weights); unconditional loads with clamped indices, since
     // conditionally assigned register arrays are placed in scratch
@@ -386,29 +392,29 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
       ((uint4*)s_scl)[min(2 * NTH + tid, npieces - 1)] = sr2;
       ((uint4*)s_scl)[min(3 * NTH + tid, npieces - 1)] = sr3;
     };
-    if (npass <= MAXP) {
+    if (npass <= MP) {
       // passes past npass repeat a valid one and are skipped; the mask is
       // opaque to the compiler so the unrolled loop keeps static register
       // indices (a bound it could see turns into a loop over a dynamically
       // indexed array in scratch)
       uint32_t live_pass = (1u << npass) - 1u;
       asm volatile("" : "+s"(live_pass));
-      ActRegs r[MAXP];
+      ActRegs r[MP];
 #pragma unroll
-      for (int p = 0; p < MAXP; ++p) act_load(min(p, npass - 1), r[p]);  // clamped; see above
+      for (int p = 0; p < MP; ++p) act_load(min(p, npass - 1), r[p]);  // clamped; see above
       load_chunk(wA, 0);
       if constexpr (decltype(two_chunks)::value) load_chunk(wB, 1);
 #pragma unroll
-      for (int p = 0; p < MAXP; ++p) act_store(p, r[p], (live_pass >> p) & 1u);
+      for (int p = 0; p < MP; ++p) act_store(p, r[p], (live_pass >> p) & 1u);
       store_scales();
     } else {
-      // MAXP passes per round trip (loads clamped, stores guarded)
-      for (int p0 = 0; p0 < npass; p0 += MAXP) {
-        ActRegs r[MAXP];
+      // MP passes per round trip (loads clamped, stores guarded)
+      for (int p0 = 0; p0 < npass; p0 += MP) {
+        ActRegs r[MP];
 #pragma unroll
-        for (int p = 0; p < MAXP; ++p) act_load(min(p0 + p, npass - 1), r[p]);
+        for (int p = 0; p < MP; ++p) act_load(min(p0 + p, npass - 1), r[p]);
 #pragma unroll
-        for (int p = 0; p < MAXP; ++p) act_store(p0 + p, r[p], p0 + p < npass);
+        for (int p = 0; p < MP; ++p) act_store(p0 + p, r[p], p0 + p < npass);
       }
       store_scales();
       load_chunk(wA, 0);
@@ -432,12 +438,22 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
     }
   };
 
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, MAXP < 2 ? MAXP : 2>;
+  using P4 = std::integral_constant<int, MAXP < 4 ? MAXP : 4>;
+  using PM = std::integral_constant<int, MAXP>;
+  auto run_prologue = [&](auto two_chunks) {
+    if (npass <= 1) prologue(two_chunks, P1{});
+    else if (npass <= 2) prologue(two_chunks, P2{});
+    else if (npass <= 4 || MAXP == 4) prologue(two_chunks, P4{});
+    else prologue(two_chunks, PM{});
+  };
   if (nchunks == 1) {
-    prologue(std::false_type{});
+    run_prologue(std::false_type{});
     compute(wA, 0);
     finish(0);
   } else {
-    prologue(std::true_type{});
+    run_prologue(std::true_type{});
     // Main loop over chunk pairs with unconditional loads; the last one to
     // three chunks are peeled.
     int c = 0;
@@ -732,7 +748,9 @@ hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi
   const int ntl = a.ntiles > 1 ? a.ntiles : 1, bt = tile_rows(a);
   const int nwg = a.splits * a.wgs_per_split;
   const dim3 grid(ntl > 1 ? (nwg + 7) / 8 * 8 * ntl : nwg), block(64 * a.nw);
-  if (ntl > a.B) return hipErrorInvalidValue;
+  // batch tiles of at most 16 rows (one matrix-core fragment; the planner
+  // makes no larger ones)
+  if (ntl > a.B || bt > 16) return hipErrorInvalidValue;
   if (a.splits != 1 && epi != kEpiPartial) return hipErrorInvalidValue;
   if (a.nw != 4 && a.nw != FUTX_GEMM_WIDE_NW && a.nw != 16) return hipErrorInvalidValue;
   const size_t lds = gemm_lds_bytes(a, nterms, G, pair);
@@ -752,8 +770,7 @@ hipError_t launch_int4_gemm(GemmArgs a, int G, int nterms, bool act_f32, int epi
   do {                                  \
     if (bt <= 4) FUTX_G(GG, 1, 1, NT, F32, EPI, PR);                   \
     else if (bt <= 8) FUTX_G(GG, 1, 2, NT, F32, EPI, PR);              \
-    else if (bt <= 16) FUTX_G(GG, 1, 4, NT, F32, EPI, PR);             \
-    else FUTX_G(GG, 2, 4, NT, F32, EPI, PR);                           \
+    else FUTX_G(GG, 1, 4, NT, F32, EPI, PR);                           \
   } while (0)
 #define FUTX_GRP(NT, F32, EPI, PR)                                        \
   do {                                                                     \
