@@ -351,12 +351,12 @@ futx_status futx::decode_block_impl(const futx_dims* dims, const futx_block_weig
     if (e2 != hipSuccess) return e2;
     switch (epi) {
       case kEpiRms:
-        if ((e2 = launch_prep_act((const float*)act, B, K, d.rms_eps, ws.act, ws.invr, s)) != hipSuccess) return e2;
+        if ((e2 = launch_prep_act((const float*)act, B, K, d.rms_eps, nullptr, ws.invr, s)) != hipSuccess) return e2;
         return launch_reduce(ws.part, p.splits, B, N, ws.invr, nullptr, out, 0, s);
       case kEpiResid:
         return launch_reduce(ws.part, p.splits, B, N, nullptr, resid, out, 0, s);
       case kEpiSwiglu:
-        if ((e2 = launch_prep_act((const float*)act, B, K, d.rms_eps, ws.act, ws.invr2, s)) != hipSuccess) return e2;
+        if ((e2 = launch_prep_act((const float*)act, B, K, d.rms_eps, nullptr, ws.invr2, s)) != hipSuccess) return e2;
         return launch_swiglu(ws.part, p.splits, B, I, ws.invr2, out_bf16, s);
     }
     return hipErrorInvalidValue;

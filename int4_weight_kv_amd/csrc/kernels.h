@@ -53,6 +53,9 @@ struct AttnArgs {
   size_t term_stride;          // elements between the bf16 terms
 };
 
+// RMS statistics of fp32 rows x[B][H] (H a multiple of 128): invr[b] =
+// 1 / sqrt(mean(x_b^2) + eps), and, when act is not null, the rows rounded
+// to bf16 in act[B][H].
 hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* act, float* invr,
                            hipStream_t st);
 hipError_t launch_reduce(const float* part, int S, int B, int N, const float* rowscale,

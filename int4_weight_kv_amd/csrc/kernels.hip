@@ -17,28 +17,39 @@ namespace futx {
 
 // ---------------------------------------------------------------- activations
 
-// act[b][:] = bf16(x[b][:]); invr[b] = 1 / sqrt(mean(x[b]^2) + eps).
+// invr[b] = 1 / sqrt(mean(x[b]^2) + eps); act[b][:] = bf16(x[b][:]) when act
+// is not null.
 // RMSNorm reading: the gain lives in the next weights and 1/r is applied to
 // the GEMM result, so the matrix-core operand is bf16(x).
-__global__ __launch_bounds__(256) void prep_act_kernel(const float* __restrict__ x, int H, float eps,
-                                                       uint16_t* __restrict__ act,
-                                                       float* __restrict__ invr) {
+__global__ __launch_bounds__(1024) void prep_act_kernel(const float* __restrict__ x, int H, float eps,
+                                                        uint16_t* __restrict__ act,
+                                                        float* __restrict__ invr) {
+  // one 1024-thread workgroup per row, 16-byte loads (H is a multiple of
+  // 128), all of a thread's loads issued before the first use
   const int b = blockIdx.x;
-  const float* xr = x + (size_t)b * H;
+  const float4* xr = (const float4*)(x + (size_t)b * H);
+  const int n4 = H >> 2;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += 256) {
-    float v = xr[c];
-    ss += v * v;
-    act[(size_t)b * H + c] = f32_to_bf16_bits(v);
+#pragma unroll 4
+  for (int i = threadIdx.x; i < n4; i += 1024) {
+    const float4 v = xr[i];
+    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    if (act) {
+      uint2 o;
+      o.x = f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+      o.y = f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+      ((uint2*)(act + (size_t)b * H))[i] = o;
+    }
   }
-  __shared__ float red[256];
-  red[threadIdx.x] = ss;
+  __shared__ float red[16];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < 16; ++w) t += red[w];
+    invr[b] = 1.0f / sqrtf(t / (float)H + eps);
   }
-  if (threadIdx.x == 0) invr[b] = 1.0f / sqrtf(red[0] / (float)H + eps);
 }
 
 // ---------------------------------------------------- split-K epilogues
@@ -61,8 +72,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
   if (idx >= B * N) return;
   const int b = idx / N, n = idx - b * N;
   const int P = physical_row(n, gateup_inter);
+  // partials summed in split order; up to 8 loads in flight per round trip
   float s = 0.f;
-  for (int sp = 0; sp < S; ++sp) s += part[((size_t)sp * B + b) * N + P];
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = s0 + j < S ? part[((size_t)(s0 + j) * B + b) * N + P] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) s += v[j];
+  }
   if (rowscale) s *= rowscale[b];
   if (resid) s += resid[idx];
   out[idx] = s;
@@ -76,10 +95,22 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
   if (c >= I) return;
   const int N = 2 * I;
   const int Pg = 32 * (c >> 4) + (c & 15), Pu = Pg + 16;
+  // partials summed in split order; up to 8 splits in flight per round trip
   float g = 0.f, u = 0.f;
-  for (int sp = 0; sp < S; ++sp) {
-    g += part[((size_t)sp * B + b) * N + Pg];
-    u += part[((size_t)sp * B + b) * N + Pu];
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float vg[8], vu[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t o = ((size_t)(s0 + j) * B + b) * N;
+      vg[j] = s0 + j < S ? part[o + Pg] : 0.f;
+      vu[j] = s0 + j < S ? part[o + Pu] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) {
+        g += vg[j];
+        u += vu[j];
+      }
   }
   g *= invr[b];
   u *= invr[b];
@@ -893,7 +924,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 
 hipError_t launch_prep_act(const float* x, int B, int H, float eps, uint16_t* act, float* invr,
                            hipStream_t st) {
-  prep_act_kernel<<<B, 256, 0, st>>>(x, H, eps, act, invr);
+  if (H % 128) return hipErrorInvalidValue;
+  prep_act_kernel<<<B, 1024, 0, st>>>(x, H, eps, act, invr);
   FUTX_LAUNCH_CHECK();
   return hipSuccess;
 }
