@@ -834,6 +834,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63;
   const int ch = t % NC, ph = t / NC;
   const float* base = apart + ((size_t)b * nq + i) * nsplit * (D + 2);
+  // The first round of partials is loaded before the sequence length is
+  // known (indices clamped to the plan's splits; partials past the
+  // sequence's own splits are never used), so the kernel waits for one
+  // memory round trip instead of two.
+  float mv[U], lv[U];
+  float4 av[U];
+  auto load_round = [&](int r0, int lim) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* pw = base + (size_t)min(r0 + ph + PH * u, lim - 1) * (D + 2);
+      mv[u] = pw[0];
+      lv[u] = pw[1];
+      av[u] = *(const float4*)(pw + 2 + 4 * ch);
+    }
+  };
+  load_round(0, nsplit);
   const int L = lens[b] + 1;  // tokens attended to
   if (L < 1 || L > tmax) {
     if (t < D) {
@@ -849,15 +865,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   float4 a = {0.f, 0.f, 0.f, 0.f};
   const int nsp = min((L + chunk - 1) / chunk, nsplit);
   for (int r0 = 0; r0 < nsp; r0 += PH * U) {
-    float mv[U], lv[U];
-    float4 av[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float* pw = base + (size_t)min(r0 + ph + PH * u, nsp - 1) * (D + 2);
-      mv[u] = pw[0];
-      lv[u] = pw[1];
-      av[u] = *(const float4*)(pw + 2 + 4 * ch);
-    }
+    if (r0 > 0) load_round(r0, nsp);
     bool ok[U];
     float mr = m;
 #pragma unroll
