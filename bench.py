@@ -378,14 +378,14 @@ def time_blocks(torch, timer, runner, layers, caches, x, reps_blocks):
 
 def sweep(torch, timer, measured, log_every=True):
     """Block times over the metric's batches: the ragged 8B block (batch 1, 4,
-    8, 16, 32; 3 layer instances), the 70B block (batch 1, 8, 32; 2
+    8, 16, 32; 3 layer instances), the 70B block (batch 1, 4, 8, 16, 32; 2
     instances) and the full 8B step (batch 1, 16)."""
     from int4_weight_kv_amd import block as DB
     from int4_weight_kv_amd import workload as W
 
     out = []
     for name, mk, batches, nl, seed0 in (("8b-ragged", W.llama8b_ragged, (1, 4, 8, 16, 32), 3, 100),
-                                         ("70b", W.llama70b, (1, 8, 32), 2, 200)):
+                                         ("70b", W.llama70b, (1, 4, 8, 16, 32), 2, 200)):
         wl0 = mk(1)
         d = wl0.dims
         layers = []
