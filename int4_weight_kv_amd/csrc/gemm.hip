@@ -54,6 +54,24 @@
 
 namespace futx {
 
+// floor(x / d) for 0 <= x < 2^20 and d >= 1, from a reciprocal taken once
+// per divisor: the fp32 estimate x * rcp(d) is within 1/4 of x / d (the
+// reciprocal is within 1 ulp, x is exact in fp32), so its truncation is off
+// by at most one, which the two corrections remove.  Six instructions
+// instead of the thirty or so of the compiler's general 32-bit division,
+// which the kernel needs for every chunk and many staging addresses.
+struct SmallDiv {
+  int d;
+  float r;
+  __device__ explicit SmallDiv(int d_) : d(d_), r(__builtin_amdgcn_rcpf((float)d_)) {}
+  __device__ int div(int x) const {
+    int q = (int)((float)x * r);
+    q -= q * d > x ? 1 : 0;
+    q += (q + 1) * d <= x ? 1 : 0;
+    return q;
+  }
+};
+
 // Register budget: at most three waves per SIMD for 4- and 8-wave
 // workgroups (more would make the compiler spill the prologue's staging
 // registers); a 16-wave workgroup (one per CU, four waves per SIMD) streams
@@ -81,22 +99,23 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   // * 8 + w % 8.  Blocks go to the 8 XCDs in turn, so the tiles of one item
   // run sit on one XCD at the same time and read the weights through its L2
   // (one HBM read).  Blocks past the plan (grid padding) leave at once.
-  int wgi = blockIdx.x, bt = 0;
+  int wgi = blockIdx.x, b0 = 0, B = a.B;  // B: rows of the tile, b0: its first row
   const int ntl = a.ntiles > 1 ? a.ntiles : 1;
   if (ntl > 1) {
-    const int r = wgi >> 3;
-    bt = r % ntl;
-    wgi = (r / ntl) * 8 + (wgi & 7);
+    const SmallDiv dt(ntl);
+    const int r = wgi >> 3, rq = __builtin_amdgcn_readfirstlane(dt.div(r)), bt = r - rq * ntl;
+    wgi = rq * 8 + (wgi & 7);
+    b0 = __builtin_amdgcn_readfirstlane(dt.div(bt * a.B));
+    B = __builtin_amdgcn_readfirstlane(dt.div((bt + 1) * a.B)) - b0;
   }
   if (wgi >= a.splits * a.wgs_per_split) return;
-  const int b0 = __builtin_amdgcn_readfirstlane(bt * a.B / ntl);                // first row of the tile
-  const int B = __builtin_amdgcn_readfirstlane((bt + 1) * a.B / ntl) - b0;       // rows of the tile
   const int KB = a.K >> 7;
-  const int split = wgi / a.wgs_per_split, wj = wgi - split * a.wgs_per_split;
+  const int split = __builtin_amdgcn_readfirstlane(SmallDiv(a.wgs_per_split).div(wgi));
+  const int wj = wgi - split * a.wgs_per_split;
   const int kb0 = split * a.kb_per_wg, kb1 = min(kb0 + a.kb_per_wg, KB);
   const int krange = kb1 - kb0;
-  const int it0 = (int)((long)wj * a.items / a.wgs_per_split);
-  const int it1 = (int)((long)(wj + 1) * a.items / a.wgs_per_split);
+  const int it0 = (int)((unsigned)wj * (unsigned)a.items / (unsigned)a.wgs_per_split);
+  const int it1 = (int)((unsigned)(wj + 1) * (unsigned)a.items / (unsigned)a.wgs_per_split);
   const int row = krange * 128 + 8;  // bf16 elements per LDS row (16 B pad)
   const int ngr = krange * 128 / G;
   constexpr int SEG = 8 * (128 / G);  // scales per (row, 8 K blocks)
@@ -117,6 +136,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   const int kbq = (krange + NW - 1) / NW;
   const int q0 = min(kb0 + wq * kbq, kb1), q1 = min(q0 + kbq, kb1);
   const int cpi = (kbq + CHK - 1) / CHK;  // chunks per item (same for every wave)
+  const SmallDiv dcpi(cpi > 0 ? cpi : 1), dbr(B * 16);
+  // item offset of chunk c (uniform)
+  auto citem = [&](int c) { return __builtin_amdgcn_readfirstlane(dcpi.div(c)); };
   const int nchunks = (it1 - it0) * cpi;
   if (nchunks == 0) return;  // the whole workgroup: before any barrier
 
@@ -126,7 +148,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   float resid_pf = 0.f;
   if constexpr (EPI == kEpiResid) {
     const int idx = min(tid, (it1 - it0) * B * 16 - 1);
-    const int il = idx / (B * 16), rem = idx - il * B * 16;
+    const int il = dbr.div(idx), rem = idx - il * B * 16;
     resid_pf = a.resid[(size_t)(b0 + (rem >> 4)) * a.N + (it0 + il) * 16 + (rem & 15)];
   }
 
@@ -135,7 +157,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   // Out-of-range K blocks of a chunk re-read the quarter's first block and
   // are weighted by zero.
   auto load_chunk = [&](uint4 (&w)[CHK][NTW], int c) {
-    const int item = it0 + c / cpi, cb = q0 + (c % cpi) * CHK;
+    const int ci = citem(c);
+    const int item = it0 + ci, cb = q0 + (c - ci * cpi) * CHK;
 #pragma unroll
     for (int i = 0; i < CHK; ++i) {
       const int kb = cb + i < q1 ? cb + i : (q0 < q1 ? q0 : kb0);
@@ -152,10 +175,11 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   // j) * 16 * (SEG / 8) + r covers row r / (SEG / 8), part r % (SEG / 8)
   constexpr int MAXS = 4;  // pieces per thread held in registers
   const int npieces = (it1 - it0) * NTW * nkb8 * 16 * (SEG / 8);
+  const SmallDiv dnkb(nkb8 > 0 ? nkb8 : 1);
   auto scl_src = [&](int p) -> const uint4* {
     const int per_blk = 16 * (SEG / 8);
     const int blk = p / per_blk, r = p - blk * per_blk;
-    const int j = blk % nkb8, iu = blk / nkb8;
+    const int iu = dnkb.div(blk), j = blk - iu * nkb8;
     const int nt = PAIR ? 2 * (it0 + iu / NTW) + iu % NTW : it0 + iu;
     return (const uint4*)(a.sc + ((size_t)nt * KB8 + b80 + j) * 16 * SEG) + r;
   };
@@ -166,12 +190,13 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   // lanes of a weight group always sit in one row.
   const int qk = (q1 - q0) * 128;
   const int nelem = B * qk;
+  const SmallDiv dqk(qk > 0 ? qk >> 7 : 1);
   const int npass = (nelem + 511) >> 9;
   // (row, element) of this lane in pass p; lanes past the end read row 0
   auto act_pos = [&](int p, int& b, int& e) {
     const int f = p * 512 + lane * 8;
     const int fc = f < nelem ? f : 0;
-    b = qk ? fc / qk : 0;
+    b = qk ? dqk.div(fc >> 7) : 0;  // qk is a multiple of 128
     e = fc - b * qk;
   };
   using ActRegs = typename std::conditional<F32, float4[2], uint4[NT]>::type;
@@ -254,8 +279,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   const uint32_t scl_lane = (uint32_t)col * SEG;
   auto compute = [&](const uint4 (&w)[CHK][NTW], int c) {
     if (q0 >= q1) return;  // empty quarter (uniform): nothing staged to read
-    const int cb = q0 + (c % cpi) * CHK;
-    const int il = c / cpi;
+    const int il = citem(c);
+    const int cb = q0 + (c - il * cpi) * CHK;
     const uint8_t* const s_act_c = (const uint8_t*)s_act;
     // A K block past the quarter was loaded from a valid block (its load is
     // unconditional, see above).  Above 8 sequences the K splits leave such
@@ -359,7 +384,8 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
         }
   };
   auto finish = [&](int c) {
-    if ((c + 1) % cpi == 0) finish_item(it0 + c / cpi, (c / cpi) & 1);
+    const int ci = citem(c);
+    if (c + 1 == (ci + 1) * cpi) finish_item(it0 + ci, ci & 1);
   };
 
   // Prologue: the activation loads (when they fit in registers) go out
@@ -484,7 +510,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
   // ---- epilogue and write-out of the workgroup's items
   const int nout = (it1 - it0) * B * 16;
   for (int idx = tid; idx < nout; idx += NTH) {
-    const int il = idx / (B * 16), rem = idx - il * B * 16, tok = rem >> 4, cc = rem & 15;
+    const int il = dbr.div(idx), rem = idx - il * B * 16, tok = rem >> 4, cc = rem & 15;
     const int n = (it0 + il) * 16 + cc;  // physical row (non-pair) / logical column (pair)
     const float o = s_out[((il * NTW) * B + tok) * 16 + cc];
     if constexpr (EPI == kEpiPartial) {
