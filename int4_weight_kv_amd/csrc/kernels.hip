@@ -632,6 +632,29 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   // sequence's first page, always allocated); clamped into the table row
   const int pg0 = t0 / kPageSize;
   const int btv = bt[lane == 63 ? 0 : min(pg0 + lane, a.mpps - 1)];
+  // 1. loads that do not depend on the sequence length go out with it: this
+  //    wave's query heads (head wv + 4 k of the group, channel lane + 64 j;
+  //    past the group: head 0 again, ignored), the new token's key and value
+  //    (every wave loads them, only the owner uses them: unconditional loads
+  //    keep the memory-counter waits exact) and the RoPE frequency of the
+  //    lane.  Below the length check they would wait for the length's round
+  //    trip before their own.
+  const float* row = a.qkv + (size_t)b * (a.nq + 2 * nkv) * D;
+  constexpr int HPW = MAXG / 4;  // query heads per wave, at most
+  float qx[HPW][D / 64];
+#pragma unroll
+  for (int k = 0; k < HPW; ++k) {
+    const int i = wv + 4 * k < G ? wv + 4 * k : 0;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) qx[k][j] = row[(size_t)(h * G + i) * D + lane + 64 * j];
+  }
+  float kx[D / 64], vx[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    kx[j] = row[(a.nq + h) * D + lane + 64 * j];
+    vx[j] = row[(a.nq + nkv + h) * D + lane + 64 * j];
+  }
+  const double inv_freq = a.inv_freq[lane % (D / 2)];
   const int pos = a.cached_lens[b];  // the new token's position
   const int T = pos + 1;             // tokens attended to
   const size_t obase = ((size_t)b * a.nq + (size_t)h * G) * D;  // output of the group's first head
@@ -649,30 +672,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
   const int nsp = (T + a.chunk - 1) / a.chunk;
   const int nwg_b = (nsp + 3) / 4;
   if (wg >= nwg_b) return;  // the whole workgroup, before any barrier
-  const float* row = a.qkv + (size_t)b * (a.nq + 2 * nkv) * D;
   const KVPtrsConst kvc{a.kv.k_codes, a.kv.v_codes, a.kv.k_scales, a.kv.v_scales, nkv};
   const int t1 = min(t0 + a.chunk, T);
   const bool owner = sp == pos / a.chunk;  // wave-uniform
   const int t1s = owner ? pos : t1;        // cached tokens of the split (the new one comes from registers)
-
-  // 1. loads: this wave's query heads (head wv + 4 k of the group, channel
-  //    lane + 64 j; past the group: head 0 again, ignored) and the new
-  //    token's key and value (every wave loads them, only the owner uses
-  //    them: unconditional loads keep the memory-counter waits exact)
-  constexpr int HPW = MAXG / 4;  // query heads per wave, at most
-  float qx[HPW][D / 64];
-#pragma unroll
-  for (int k = 0; k < HPW; ++k) {
-    const int i = wv + 4 * k < G ? wv + 4 * k : 0;
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) qx[k][j] = row[(size_t)(h * G + i) * D + lane + 64 * j];
-  }
-  float kx[D / 64], vx[D / 64];
-#pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    kx[j] = row[(a.nq + h) * D + lane + 64 * j];
-    vx[j] = row[(a.nq + nkv + h) * D + lane + 64 * j];
-  }
 
   // 2. the split's first two pages go out first (a wave with nothing to
   //    scan reads the sequence's first page and ignores it: unconditional
@@ -691,7 +694,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a) {
     issue_page<D>(kvc, p1, h, b0, b1);
   }
   float cs, sn;  // cos / sin of frequency index lane % (D / 2), shared by the key and the queries
-  rope_cs_inv(pos, a.inv_freq[lane % (D / 2)], &cs, &sn);
+  rope_cs_inv(pos, inv_freq, &cs, &sn);
   TokenCodes<D> tok;
   if (owner) {
     rope_lane_cs<D>(kx, cs, sn);
