@@ -610,11 +610,12 @@ static GemmPlan2 plan_tile(int N, int K, int G, int B, int nterms, int epi, int 
   // Below 5 sequences the same shape wins for large projections, where the
   // 4-wave workgroups staging B activation rows each leave one or two
   // workgroups per CU (measured on MI355X, 70B: O at batch 4 25.8 -> 15.6
-  // us, gate/up at batch 1 53 -> 45 us, down at batch 2 45 -> 28 us), but
-  // not for small ones at small batch (8B O at batch 2 6.4 -> 7.9 us).  The
-  // weight bytes per CU above which it is taken fall with the batch.
+  // us, gate/up at batch 1 53 -> 45 us, down at batch 2 45 -> 28 us, QKV at
+  // batch 1 14.3 -> 13.4 us), but not for small ones at small batch (8B O
+  // at batch 2 6.4 -> 7.9 us): from batch 4 always, below with at least
+  // 128 KiB of weights per CU (and K >= 64 blocks at batch 1).
   const long wcu = (long)N * K / 2 / cus;
-  const bool deep = B >= 4 || (B >= 2 && wcu >= (128L << 10)) || (KB >= 64 && wcu >= (256L << 10));
+  const bool deep = B >= 4 || (wcu >= (128L << 10) && (B >= 2 || KB >= 64));
   // A plan that needs more workgroups than CUs (the items of a share do not
   // fit the LDS) runs a second, partial round; K splits beyond the LDS
   // minimum (kEpiPartial) shrink the staged range until one round holds
