@@ -287,9 +287,9 @@ __attribute__((amdgpu_waves_per_eu(NW == 16 ? 4 : 1, NW == 16 ? 4 : 3))) void in
     // slots in most chunks, and they are skipped: the branch is wave-uniform
     // and holds no memory load (measured on MI355X: the 8B O projection at
     // batch 32 43 -> 25 us, the whole 70B block at batch 32 875 -> 666 us).
-    // Up to 8 sequences every wave's share is a whole number of chunks, and
-    // the branch-free form (weight 0) is kept: the branch cost 0.3-0.5 us on
-    // the 8B O and gate/up projections at batch 1.
+    // Up to 8 sequences (where such slots are rare) the branch-free form
+    // (weight 0) is kept: the branch cost 0.3-0.5 us on the 8B O and gate/up
+    // projections at batch 1.
     constexpr bool kSkipPast = NR == 4;
 #pragma unroll
     for (int i = 0; i < CHK; ++i) {
