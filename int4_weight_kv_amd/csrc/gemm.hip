@@ -756,6 +756,18 @@ static GemmPlan2 choose(int N, int K, int G, int B, int nterms, int epi, bool* f
   if (*fused && B <= 8) return best;
   double pc;
   const GemmPlan2 q = best_partial(N, K, G, B, nterms, &pc);
+  // Up to 8 sequences, a K split that leaves 16-wave chunks half empty (one
+  // K block per wave) loses to the fused plan in two batch tiles when that
+  // fits (measured on MI355X, 70B O at batch 8 23.2 -> 20.5 us, batch 5
+  // 22.6 -> 18.9); with full chunks the K split stays (8B down, 70B gate/up
+  // and down were slower in two tiles).
+  if (!*fused && B <= 8 && B >= 2 && q.nw == 16 && (q.kb_per_wg + 15) / 16 < 2) {
+    const GemmPlan2 f = plan_tiled(N, K, G, B, nterms, epi, 2);
+    if (tile_fits(f, B, G, nterms, epi)) {
+      *fused = true;
+      return f;
+    }
+  }
   if (!*fused || pc < bc) {
     *fused = false;
     return q;
